@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Lighthouse attention layer benchmark on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input: pool+score,
+chunked top-K, map, gather, causal attention, scatter (forward), then scatter backward, the
+two attention backward passes and gather+pool backward.  The steps run through the library's
+stage entry points (the same kernels lh_forward / lh_backward launch, in the same order) with
+HIP events recorded between stages on the launch stream, so every kernel's time comes from
+the timed steps themselves.  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Lighthouse fwd+bwd tokens/sec/layer at 512K on 1 GPU; % HBM and MFMA peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(w, info):
+    """Per-launch algorithmic work of each stage (bytes for HBM stages, flops for attention).
+
+    Each stage counts its own inputs read once and outputs written once, at the dtypes the
+    path stores: pooled levels bf16, scores float32, indices int32, gathered rows bf16,
+    Og / LSE / gathered gradients float32.
+    """
+    B, N, H, D = w.batch, w.n_tokens, w.heads, w.head_dim
+    S, Sp, P, P1, K = (info.gathered_len, info.gathered_pad, info.pyramid_total,
+                       info.pooled_rows, info.sel_total)
+    e = 2 if w.dtype == "bf16" else 4  # token-tensor element size
+    BH = B * H
+    pairs = BH * S * (S + 1) / 2
+    by = {
+        "pool_score": 3 * B * N * H * D * e + 3 * B * P1 * H * D * 2 + BH * (P - N) * 4,
+        "topk": BH * (P - N) * 4 + BH * K * 4,
+        "build_map": BH * K * 4 + BH * P * 4 + BH * S * 8,
+        "gather": BH * S * 4 + 3 * BH * S * D * 2 + 6 * BH * S * D * 2,
+        "scatter": BH * S * D * 4 + B * N * H * D * e + BH * N * w.levels * 4,
+        "scatter_bwd": B * N * H * D * e + BH * S * 4 + BH * S * D * 4 + 2 * BH * S * D * 2
+                       + BH * S * 4,
+        "gather_pool_bwd": 3 * BH * S * D * 4 + 3 * B * N * H * D * e + BH * N * w.levels * 4,
+    }
+    fl = {
+        "attn_fwd": 2 * 2 * D * pairs,        # Q K^T and P V
+        "attn_bwd_dkdv": 4 * 2 * D * pairs,   # Q K^T, dO V^T, P^T dO, dS^T Q
+        "attn_bwd_dq": 1 * 2 * D * pairs,     # dS K (its two recomputed products are overhead)
+    }
+    return by, fl
+
+
+def time_staged(layer, steps, warmup, torch):
+    names = [n for n, _ in layer.stages_fwd + layer.stages_bwd]
+    stages = layer.stages_fwd + layer.stages_bwd
+    for i in range(warmup):
+        layer.run(stages)
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{warmup} done")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record()
+        layer.run(stages, between=lambda i, n, s=s: ev[s][i + 1].record())
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: 0.0 for n in names}
+    for s in range(steps):
+        for i, n in enumerate(names):
+            per[n] += ev[s][i].elapsed_time(ev[s][i + 1])
+    per = {n: v / steps for n, v in per.items()}
+    gpu_step = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)) / steps
+    return wall / steps * 1e3, gpu_step, per
+
+
+def time_monolithic(torch, ops, cfg, t, steps, with_bwd=True):
+    bufs = ops.Buffers(cfg)
+    y = torch.empty_like(t["q"])
+    dx = [torch.empty_like(t["q"]) for _ in range(3)]
+
+    def step():
+        ops.lh_forward(cfg, t["q"], t["k"], t["v"], bufs=bufs, y=y)
+        if with_bwd:
+            ops.lh_backward(cfg, bufs, t["dy"], *dx)
+
+    step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    del bufs
+    return a.elapsed_time(b) / steps
+
+
+def cpu_baseline(w, x):
+    """The oracle, as it stands, on head 0 of batch 0 of the same inputs (fwd + bwd)."""
+    import numpy as np
+
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    ocfg = O.Config(w.levels, w.pool, w.k, w.chunk)
+    q, k, v, dy = (x[n][0, :, 0].astype(np.float64) for n in ("q", "k", "v", "dy"))
+    t0 = time.perf_counter()
+    _, st = O.head_forward(q, k, v, ocfg)
+    O.head_backward(dy, st, ocfg)
+    t = time.perf_counter() - t0
+    # heads are independent and the oracle runs them one after another
+    return {"value": w.batch * w.n_tokens / (t * w.heads * w.batch), "unit": "tokens/s/layer",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"head 0 of {w.heads} (batch 0) of the {w.name} workload, forward + "
+                      f"backward, {t:.1f} s; scaled by the head count"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="lh-512k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention baseline")
+    ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this "
+              "build (the multi-GPU sharding is a design note, not code).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from hierarchical_sparse_attention_lh_amd import _lib, ops, synth
+
+    w = synth.WORKLOADS[args.workload]
+    log(f"workload {w}")
+    t0 = time.perf_counter()
+    x = synth.workload_inputs(w, with_grad=True)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = {n: torch.from_numpy(a).to("cuda").to(dt) for n, a in x.items()}
+    torch.cuda.synchronize()
+    cfg = ops.config_for(w)
+    info = ops.lh_plan(cfg)
+    layer = ops.StagedLayer(cfg, t["q"], t["k"], t["v"], t["dy"])
+    log(f"S = {info.gathered_len}, buffers ready; hip runtimes: {_lib.hip_runtimes_mapped()}")
+
+    wall_ms, gpu_ms, per = time_staged(layer, args.steps, args.warmup, torch)
+    ms = max(wall_ms, gpu_ms)
+    tokens = w.batch * w.n_tokens
+    log(f"staged step: {ms:.3f} ms ({per})")
+    fwd_names = [n for n, _ in layer.stages_fwd]
+    fwd_ms = sum(per[n] for n in fwd_names)
+    mono_fb = time_monolithic(torch, ops, cfg, t, max(1, args.steps // 2))
+    mono_f = time_monolithic(torch, ops, cfg, t, max(1, args.steps // 2), with_bwd=False)
+    log(f"lh_forward+lh_backward: {mono_fb:.3f} ms; lh_forward: {mono_f:.3f} ms")
+    del layer
+    torch.cuda.empty_cache()
+
+    by, fl = algorithmic(w, info)
+    stages = {}
+    for n, v in per.items():
+        if n in fl:
+            stages[n] = {"ms": round(v, 4), "tflops": round(fl[n] / (v * 1e-3) / 1e12, 2),
+                         "mfma_frac": round(fl[n] / (v * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        else:
+            stages[n] = {"ms": round(v, 4), "gbs": round(by[n] / (v * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(by[n] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    hbm_names = [n for n in per if n in by]
+    hbm_bytes = sum(by[n] for n in hbm_names)
+    hbm_ms = sum(per[n] for n in hbm_names)
+    dom = max(per, key=per.get)
+    if dom in fl:
+        ach = fl[dom] / (per[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "avg_ms": round(per[dom], 4)}
+    else:
+        ach = by[dom] / (per[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "avg_ms": round(per[dom], 4)}
+
+    dense = None
+    if not args.no_dense:
+        dw = synth.Workload("dense-" + w.name, w.batch, w.n_tokens, w.heads, w.head_dim, w.dtype,
+                            1, w.pool, 0, w.chunk, w.seed, True)
+        dcfg = ops.config_for(dw)
+        log("timing the dense causal attention baseline (levels = 1, S = N)")
+        d_fb = time_monolithic(torch, ops, dcfg, t, 1)
+        d_f = time_monolithic(torch, ops, dcfg, t, 1, with_bwd=False)
+        dense = {"fwd_ms": round(d_f, 2), "fwd_bwd_ms": round(d_fb, 2),
+                 "speedup_fwd": round(d_f / mono_f, 2), "speedup_fwd_bwd": round(d_fb / mono_fb, 2)}
+        log(f"dense: {dense}")
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one head")
+        cpu = cpu_baseline(w, x)
+        log(f"cpu baseline: {cpu}")
+
+    out = {
+        "metric": METRIC, "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s/layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_tokens": w.n_tokens, "heads": w.heads,
+                   "head_dim": w.head_dim, "levels": w.levels, "pool": w.pool, "k": w.k,
+                   "chunk": w.chunk, "gathered_len": info.gathered_len,
+                   "input_dtype": w.dtype, "seed": w.seed},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "forward_tokens_per_s": round(tokens / (fwd_ms * 1e-3), 1),
+        "forward_ms": round(fwd_ms, 4),
+        "monolithic_ms": {"fwd_bwd": round(mono_fb, 4), "fwd": round(mono_f, 4)},
+        "hbm_stages": {"bytes": int(hbm_bytes), "ms": round(hbm_ms, 4),
+                       "gbs": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9, 1),
+                       "frac": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "stages": stages,
+        "dense_baseline": dense,
+    }
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,87 @@
+// Internal declarations shared by the host side (lh_api.cpp) and the HIP kernels.
+// Not part of the public ABI; the public interface is include/lh_api.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lh_api.h"
+
+namespace lh {
+
+// Level table derived on the host from an lh_config (closed forms only), passed by value
+// to kernels.  Level l has n[l] = N / p^l entries; pyramid id of (l, j) = off[l] + j.
+struct Levels {
+  int32_t L, p;
+  int64_t B, N;
+  int32_t H, D;
+  int64_t n[LH_MAX_LEVELS];     // entries per level
+  int64_t pw[LH_MAX_LEVELS];    // p^l (tokens per entry)
+  int64_t off[LH_MAX_LEVELS];   // pyramid offsets
+  int64_t poff[LH_MAX_LEVELS];  // rows of level l (>= 1) inside the pooled tensors
+  int64_t keff[LH_MAX_LEVELS];  // kept entries at selected levels (0 elsewhere)
+  int64_t nchunk[LH_MAX_LEVELS];
+  int64_t width[LH_MAX_LEVELS]; // chunk width
+  int64_t soff[LH_MAX_LEVELS];  // offset of the level's kept indices in sel
+  int64_t P;                    // pyramid total
+  int64_t P1;                   // pooled rows (levels >= 1)
+  int64_t K;                    // sel_total
+  int64_t S;                    // gathered length
+};
+
+// ---------------------------------------------------------------- bf16 helpers
+// bfloat16 values are carried as raw 16-bit patterns.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// float32 -> bfloat16, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// Two floats -> packed bf16 pair (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// Gathered-domain tensors are stored with their sequence length padded to a multiple of
+// 128 (one forward query tile); padding rows are written as finite values (zeros).
+inline int64_t padded_len(int64_t S) { return (S + 127) / 128 * 128; }
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are already validated.
+hipError_t launch_pool_score(const Levels& lv, int32_t in_f32, const void* q, const void* k,
+                             const void* v, void* pq, void* pk, void* pv, int32_t out_f32,
+                             float* scores, hipStream_t st);
+hipError_t launch_topk(const Levels& lv, const float* scores, int32_t* sel, hipStream_t st);
+hipError_t launch_build_map(const Levels& lv, const int32_t* sel, int32_t* gmap, int32_t* inv,
+                            hipStream_t st);
+hipError_t launch_gather(const Levels& lv, int32_t in_f32, const void* x[3], const void* px[3],
+                         int32_t pooled_f32, const int32_t* gmap, void* const rows[3],
+                         void* const trans[3], hipStream_t st);
+hipError_t launch_attn_fwd(int64_t B, int64_t H, int64_t S, int32_t D, float scale,
+                           const void* q, const void* k, const void* vt, float* o, float* lse,
+                           hipStream_t st);
+hipError_t launch_attn_bwd(int64_t B, int64_t H, int64_t S, int32_t D, float scale,
+                           const void* q, const void* k, const void* v, const void* qt,
+                           const void* kt, const float* lse, const float* delta,
+                           const void* dout, const void* doutt, float* dq, float* dk,
+                           float* dv, hipStream_t st);
+// pass: 1 = key pass only, 2 = query pass only, 3 = both
+hipError_t launch_attn_bwd_pass(int pass, int64_t B, int64_t H, int64_t S, int32_t D,
+                                float scale, const void* q, const void* k, const void* v,
+                                const void* qt, const void* kt, const float* lse,
+                                const float* delta, const void* dout, const void* doutt,
+                                float* dq, float* dk, float* dv, hipStream_t st);
+hipError_t launch_scatter(const Levels& lv, int32_t out_f32, const int32_t* inv,
+                          const float* og, void* y, hipStream_t st);
+hipError_t launch_scatter_bwd(const Levels& lv, int32_t in_f32, const int32_t* gmap,
+                              const float* og, const void* dy, void* dog, void* dogt,
+                              float* delta, hipStream_t st);
+hipError_t launch_gather_pool_bwd(const Levels& lv, int32_t out_f32, const int32_t* inv,
+                                  const float* dqg, const float* dkg, const float* dvg,
+                                  void* dq, void* dk, void* dv, hipStream_t st);
+
+}  // namespace lh

@@ -1,0 +1,198 @@
+// Stage 1+2: symmetric pyramid pool of Q, K, V and the per-head l2 score of pooled keys.
+//
+// [WS] wispaper.ai, "Lighthouse Attention：预训练长文本的高速公路，训练提速 21 倍且无损恢复",
+// section "核心方法：金字塔池化与“外部选择”", item 1: Q, K and V are average-pooled together
+// into a multi-level pyramid.  [EN] encorp.ai, "Услуги по внедряване на AI задават правилния
+// въпрос за Lighthouse Attention", section "Как four-stage pipeline остава бърз, без да чупи
+// градиентите?": entries are scored with per-head l2 norms (reading: of the pooled key row).
+//
+// Design (HBM-bound scan): one thread owns 8 consecutive columns of a token row (one 16-byte
+// bf16 load per token) and walks one coarsest block of p^(L-1) tokens, keeping a float32
+// running mean per level in registers.  Every time a level-l block closes, the thread writes
+// its 8 pooled columns; for the key stream the 8 squares are summed in float64 and reduced
+// over the D/8 lanes of the head with cross-lane shuffles, and one lane writes the score.
+// A wave reads 64 x 16 B = 1 KB of one token row per step: fully coalesced.  Q, K and V are
+// separate grid rows (blockIdx.y) so the three streams run concurrently.
+#include "lh_internal.h"
+
+namespace lh {
+namespace {
+
+__device__ __forceinline__ void load8(const uint16_t* p, float (&o)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ void load8(const float* p, float (&o)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+  o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
+__device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8]) {
+  uint4 u;
+  u.x = pack_bf16x2(v[0], v[1]);
+  u.y = pack_bf16x2(v[2], v[3]);
+  u.z = pack_bf16x2(v[4], v[5]);
+  u.w = pack_bf16x2(v[6], v[7]);
+  *reinterpret_cast<uint4*>(p) = u;
+}
+
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+template <typename Tin, typename Tout>
+struct Ctx {
+  const Tin* x;    // this thread's column in token row 0 of its batch
+  Tout* px;        // this thread's column in pooled row 0 of its batch (or null)
+  float* sc;       // scores of this (batch, head) (or null)
+  int64_t row;     // elements per token row (H * D)
+  int p;
+  float inv_p;
+  int hd8;         // D / 8 lanes per head
+  bool writer;     // first lane of the head
+};
+
+template <typename Tin, typename Tout>
+__device__ __forceinline__ void emit(const Ctx<Tin, Tout>& c, const Levels& lv, int level,
+                                     int64_t j, const float (&v)[8]) {
+  if (c.px) store8(c.px + (lv.poff[level] + j) * c.row, v);
+  if (c.sc) {
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += static_cast<double>(v[i]) * static_cast<double>(v[i]);
+    for (int m = 1; m < c.hd8; m <<= 1) ss += __shfl_xor(ss, m);
+    if (c.writer) c.sc[lv.off[level] + j] = static_cast<float>(sqrt(ss));
+  }
+}
+
+// Mean over the p tokens starting at token t0 (level 1); loads are issued four at a time so
+// that several 16-byte requests per thread are in flight.
+template <typename Tin, typename Tout>
+__device__ __forceinline__ void level1(const Ctx<Tin, Tout>& c, int64_t t0, float (&out)[8]) {
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int i0 = 0; i0 < c.p; i0 += 4) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u < c.p) load8(c.x + (t0 + i0 + u) * c.row, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u < c.p) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += v[u][e];
+      }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = acc[e] * c.inv_p;
+}
+
+template <int LVL, typename Tin, typename Tout>
+__device__ __forceinline__ void pool_block(const Ctx<Tin, Tout>& c, const Levels& lv, int64_t t0,
+                                           float (&out)[8]) {
+  if constexpr (LVL == 1) {
+    level1(c, t0, out);
+  } else {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    const int64_t span = lv.pw[LVL - 1];
+    for (int i = 0; i < c.p; ++i) {
+      float ch[8];
+      pool_block<LVL - 1>(c, lv, t0 + i * span, ch);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += ch[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = acc[e] * c.inv_p;
+  }
+  emit(c, lv, LVL, t0 / lv.pw[LVL], out);
+}
+
+template <int L, typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void pool_score_kernel(Levels lv, const Tin* __restrict__ q,
+                                                         const Tin* __restrict__ k,
+                                                         const Tin* __restrict__ v,
+                                                         Tout* pq, Tout* pk, Tout* pv,
+                                                         float* scores) {
+  const int stream = blockIdx.y;  // 0 = Q, 1 = K, 2 = V
+  const Tin* x = stream == 0 ? q : (stream == 1 ? k : v);
+  Tout* px = stream == 0 ? pq : (stream == 1 ? pk : pv);
+  if (px == nullptr && stream != 1) return;
+
+  const int64_t G = static_cast<int64_t>(lv.H) * lv.D / 8;  // column groups per row
+  const int64_t T = lv.pw[L - 1];                              // tokens per coarsest block
+  const int64_t tiles = lv.N / T;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= lv.B * tiles * G) return;
+  const int64_t g = gid % G;
+  const int64_t tt = gid / G;
+  const int64_t tile = tt % tiles;
+  const int64_t b = tt / tiles;
+  const int hd8 = lv.D / 8;
+  const int64_t h = g / hd8;
+
+  Ctx<Tin, Tout> c;
+  c.row = G * 8;
+  c.x = x + b * lv.N * c.row + g * 8;
+  c.px = px ? px + b * lv.P1 * c.row + g * 8 : nullptr;
+  c.sc = stream == 1 ? scores + (b * lv.H + h) * lv.P : nullptr;
+  c.p = lv.p;
+  c.inv_p = 1.0f / static_cast<float>(lv.p);
+  c.hd8 = hd8;
+  c.writer = (g % hd8) == 0;
+
+  float out[8];
+  pool_block<L - 1>(c, lv, tile * T, out);
+}
+
+template <typename Tin, typename Tout>
+hipError_t dispatch(const Levels& lv, const void* q, const void* k, const void* v, void* pq,
+                    void* pk, void* pv, float* scores, hipStream_t st) {
+  const int64_t G = static_cast<int64_t>(lv.H) * lv.D / 8;
+  const int64_t total = lv.B * (lv.N / lv.pw[lv.L - 1]) * G;
+  dim3 grid(static_cast<unsigned>((total + 255) / 256), 3);
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, lv, static_cast<const Tin*>(q),
+                       static_cast<const Tin*>(k), static_cast<const Tin*>(v),
+                       static_cast<Tout*>(pq), static_cast<Tout*>(pk), static_cast<Tout*>(pv),
+                       scores);
+  };
+  switch (lv.L) {
+    case 2: args(pool_score_kernel<2, Tin, Tout>); break;
+    case 3: args(pool_score_kernel<3, Tin, Tout>); break;
+    case 4: args(pool_score_kernel<4, Tin, Tout>); break;
+    case 5: args(pool_score_kernel<5, Tin, Tout>); break;
+    case 6: args(pool_score_kernel<6, Tin, Tout>); break;
+    case 7: args(pool_score_kernel<7, Tin, Tout>); break;
+    case 8: args(pool_score_kernel<8, Tin, Tout>); break;
+    default: return hipSuccess;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pool_score(const Levels& lv, int32_t in_f32, const void* q, const void* k,
+                             const void* v, void* pq, void* pk, void* pv, int32_t out_f32,
+                             float* scores, hipStream_t st) {
+  if (lv.L < 2) return hipSuccess;
+  if (in_f32) {
+    return out_f32 ? dispatch<float, float>(lv, q, k, v, pq, pk, pv, scores, st)
+                   : dispatch<float, uint16_t>(lv, q, k, v, pq, pk, pv, scores, st);
+  }
+  return out_f32 ? dispatch<uint16_t, float>(lv, q, k, v, pq, pk, pv, scores, st)
+                 : dispatch<uint16_t, uint16_t>(lv, q, k, v, pq, pk, pv, scores, st);
+}
+
+}  // namespace lh

@@ -1,0 +1,266 @@
+// Stage 5 and the token-side adjoints: scatter, scatter backward, gather+pool backward.
+//
+// [EN] encorp.ai, "Услуги по внедряване на AI задават правилния въпрос за Lighthouse
+// Attention", section "Как four-stage pipeline остава бърз, без да чупи градиентите?": the
+// attention outputs are spread back over the original positions with an offset that keeps
+// causality, and gradients return to Q, K, V only through the gathered values.  [WS]
+// wispaper.ai, "Lighthouse Attention：预训练长文本的高速公路，训练提速 21 倍且无损恢复",
+// architecture figure caption under "核心方法：金字塔池化与“外部选择”": scatter-back closes
+// the pipeline.
+//
+// Readings: entry (l, j) (causal position e = (j+1) p^l - 1) is added to tokens
+// [e, e + p^l - 1]; tokens reached by nothing are 0.  Pool backward hands each source token
+// of a gathered pooled entry 1/p^l of its gradient.
+//
+// Design: all three kernels are pull-based (each output element is written by exactly one
+// thread, no atomics) and HBM-bound.  A workgroup owns 32 consecutive tokens (or slots) of
+// one head; D/8 lanes per row each move 8 columns with 16-/32-byte vectors.  Per token the
+// L level lookups go through `inv` ([B, H, P]); coarse entries repeat across neighbouring
+// tokens and hit in cache.  Scatter backward sums each slot's token span in float32, rounds
+// once to bf16, writes the row layout directly and the transposed layout through LDS, and
+// fuses Delta = rowsum(dO * O) for the attention backward.
+#include "lh_internal.h"
+
+namespace lh {
+namespace {
+
+__device__ __forceinline__ void ld8(const float* p, float (&o)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+  o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
+__device__ __forceinline__ void ld8(const uint16_t* p, float (&o)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ void st8(float* p, const float (&v)[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+__device__ __forceinline__ void st8(uint16_t* p, const float (&v)[8]) {
+  uint4 u;
+  u.x = pack_bf16x2(v[0], v[1]);
+  u.y = pack_bf16x2(v[2], v[3]);
+  u.z = pack_bf16x2(v[4], v[5]);
+  u.w = pack_bf16x2(v[6], v[7]);
+  *reinterpret_cast<uint4*>(p) = u;
+}
+
+constexpr int kTok = 32;  // tokens (or slots) per workgroup
+
+// ----------------------------------------------------------------------------- scatter
+template <int D, typename Tout>
+__global__ __launch_bounds__(256) void scatter_kernel(Levels lv, int64_t Sp,
+                                                      const int32_t* __restrict__ inv,
+                                                      const float* __restrict__ og,
+                                                      Tout* __restrict__ y) {
+  constexpr int G = D / 8, TPP = 256 / G;  // lanes per row, tokens per pass
+  const int64_t bh = blockIdx.y;
+  const int64_t b = bh / lv.H, h = bh % lv.H;
+  const int g = threadIdx.x % G;
+  const int64_t row = static_cast<int64_t>(lv.H) * D;
+  const int32_t* iv = inv + bh * lv.P;
+  const float* ob = og + bh * Sp * D;
+#pragma unroll
+  for (int pass = 0; pass < kTok / TPP; ++pass) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kTok + pass * TPP + threadIdx.x / G;
+    if (t >= lv.N) continue;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int l = 0; l < lv.L; ++l) {
+      const int64_t j = (t + 1) / lv.pw[l] - 1;
+      if (j < 0) continue;
+      const int32_t s = iv[lv.off[l] + j];
+      if (s < 0 || s >= lv.S) continue;
+      float v[8];
+      ld8(ob + static_cast<int64_t>(s) * D + g * 8, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += v[e];
+    }
+    st8(y + (b * lv.N + t) * row + h * D + g * 8, acc);
+  }
+}
+
+// -------------------------------------------------------------------- scatter backward
+template <int D, typename Tin>
+__global__ __launch_bounds__(256) void scatter_bwd_kernel(
+    Levels lv, int64_t Sp, const int32_t* __restrict__ gmap, const float* __restrict__ og,
+    const Tin* __restrict__ dy, uint16_t* __restrict__ dog, uint16_t* __restrict__ dogt,
+    float* __restrict__ delta) {
+  constexpr int G = D / 8, SPP = 256 / G;
+  constexpr int TS = 64;       // slots per workgroup (transposed writes are 128 B)
+  constexpr int LR = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[TS * LR];
+  const int64_t bh = blockIdx.y;
+  const int64_t b = bh / lv.H, h = bh % lv.H;
+  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * TS;
+  const int g = threadIdx.x % G;
+  const int64_t row = static_cast<int64_t>(lv.H) * D;
+  const Tin* yb = dy + b * lv.N * row + h * D + g * 8;
+#pragma unroll
+  for (int pass = 0; pass < TS / SPP; ++pass) {
+    const int sl = pass * SPP + threadIdx.x / G;
+    const int64_t s = s0 + sl;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    const int32_t id = s < lv.S ? gmap[bh * Sp + s] : -1;
+    if (id >= 0 && id < lv.P) {
+      int l = 0;
+      while (l < lv.L - 1 && id >= lv.off[l + 1]) ++l;
+      const int64_t j = id - lv.off[l];
+      const int64_t lo = (j + 1) * lv.pw[l] - 1;
+      const int64_t hi = lo + lv.pw[l] < lv.N ? lo + lv.pw[l] : lv.N;
+      for (int64_t t = lo; t < hi; ++t) {
+        float v[8];
+        ld8(yb + t * row, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += v[e];
+      }
+    }
+    // round once to bf16; Delta uses the rounded values, as the attention backward does
+    float r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = bf16_to_f32(f32_to_bf16(acc[e]));
+    uint16_t* dst = dog + (bh * Sp + s) * D + g * 8;
+    st8(dst, r);
+    *reinterpret_cast<uint4*>(&tile[sl * LR + g * 8]) = *reinterpret_cast<const uint4*>(dst);
+    float o[8];
+    ld8(og + (bh * Sp + s) * D + g * 8, o);
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part = fmaf(r[e], o[e], part);
+    for (int m = 1; m < G; m <<= 1) part += __shfl_xor(part, m);
+    if (g == 0) delta[bh * Sp + s] = s < lv.S ? part : 0.f;
+  }
+  __syncthreads();
+  for (int w = threadIdx.x; w < D * (TS / 8); w += 256) {
+    const int d = w / (TS / 8);
+    const int sg = (w % (TS / 8)) * 8;
+    uint32_t pk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      pk[u] = static_cast<uint32_t>(tile[(sg + 2 * u) * LR + d]) |
+              (static_cast<uint32_t>(tile[(sg + 2 * u + 1) * LR + d]) << 16);
+    *reinterpret_cast<uint4*>(dogt + (bh * D + d) * Sp + s0 + sg) =
+        make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  }
+}
+
+// ------------------------------------------------------------- gather + pool backward
+template <int D, typename Tout>
+__global__ __launch_bounds__(256) void gather_pool_bwd_kernel(
+    Levels lv, int64_t Sp, const int32_t* __restrict__ inv, const float* __restrict__ g0,
+    const float* __restrict__ g1, const float* __restrict__ g2, Tout* __restrict__ d0,
+    Tout* __restrict__ d1, Tout* __restrict__ d2) {
+  constexpr int G = D / 8, TPP = 256 / G;
+  const int64_t bh = blockIdx.y;
+  const int64_t b = bh / lv.H, h = bh % lv.H;
+  const int which = blockIdx.z;
+  const float* gx = which == 0 ? g0 : (which == 1 ? g1 : g2);
+  Tout* dx = which == 0 ? d0 : (which == 1 ? d1 : d2);
+  const int g = threadIdx.x % G;
+  const int64_t row = static_cast<int64_t>(lv.H) * D;
+  const int32_t* iv = inv + bh * lv.P;
+  const float* gb = gx + bh * Sp * D;
+#pragma unroll
+  for (int pass = 0; pass < kTok / TPP; ++pass) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kTok + pass * TPP + threadIdx.x / G;
+    if (t >= lv.N) continue;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    float w = 1.0f;
+    for (int l = 0; l < lv.L; ++l) {
+      const int32_t s = iv[lv.off[l] + t / lv.pw[l]];
+      if (s >= 0 && s < lv.S) {
+        float v[8];
+        ld8(gb + static_cast<int64_t>(s) * D + g * 8, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(v[e], w, acc[e]);
+      }
+      w /= static_cast<float>(lv.p);
+    }
+    st8(dx + (b * lv.N + t) * row + h * D + g * 8, acc);
+  }
+}
+
+template <typename Tout>
+hipError_t scatter_t(const Levels& lv, const int32_t* inv, const float* og, void* y,
+                     hipStream_t st) {
+  const int64_t Sp = padded_len(lv.S);
+  dim3 grid(static_cast<unsigned>((lv.N + kTok - 1) / kTok), static_cast<unsigned>(lv.B * lv.H));
+  if (lv.D == 64)
+    hipLaunchKernelGGL((scatter_kernel<64, Tout>), grid, dim3(256), 0, st, lv, Sp, inv, og,
+                       static_cast<Tout*>(y));
+  else
+    hipLaunchKernelGGL((scatter_kernel<128, Tout>), grid, dim3(256), 0, st, lv, Sp, inv, og,
+                       static_cast<Tout*>(y));
+  return hipGetLastError();
+}
+
+template <typename Tin>
+hipError_t scatter_bwd_t(const Levels& lv, const int32_t* gmap, const float* og, const void* dy,
+                         void* dog, void* dogt, float* delta, hipStream_t st) {
+  const int64_t Sp = padded_len(lv.S);
+  dim3 grid(static_cast<unsigned>(Sp / 64), static_cast<unsigned>(lv.B * lv.H));
+  auto* a = static_cast<uint16_t*>(dog);
+  auto* at = static_cast<uint16_t*>(dogt);
+  if (lv.D == 64)
+    hipLaunchKernelGGL((scatter_bwd_kernel<64, Tin>), grid, dim3(256), 0, st, lv, Sp, gmap, og,
+                       static_cast<const Tin*>(dy), a, at, delta);
+  else
+    hipLaunchKernelGGL((scatter_bwd_kernel<128, Tin>), grid, dim3(256), 0, st, lv, Sp, gmap, og,
+                       static_cast<const Tin*>(dy), a, at, delta);
+  return hipGetLastError();
+}
+
+template <typename Tout>
+hipError_t gpb_t(const Levels& lv, const int32_t* inv, const float* a, const float* b,
+                 const float* c, void* x, void* y, void* z, hipStream_t st) {
+  const int64_t Sp = padded_len(lv.S);
+  dim3 grid(static_cast<unsigned>((lv.N + kTok - 1) / kTok), static_cast<unsigned>(lv.B * lv.H),
+            3);
+  if (lv.D == 64)
+    hipLaunchKernelGGL((gather_pool_bwd_kernel<64, Tout>), grid, dim3(256), 0, st, lv, Sp, inv,
+                       a, b, c, static_cast<Tout*>(x), static_cast<Tout*>(y),
+                       static_cast<Tout*>(z));
+  else
+    hipLaunchKernelGGL((gather_pool_bwd_kernel<128, Tout>), grid, dim3(256), 0, st, lv, Sp, inv,
+                       a, b, c, static_cast<Tout*>(x), static_cast<Tout*>(y),
+                       static_cast<Tout*>(z));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scatter(const Levels& lv, int32_t out_f32, const int32_t* inv,
+                          const float* og, void* y, hipStream_t st) {
+  return out_f32 ? scatter_t<float>(lv, inv, og, y, st) : scatter_t<uint16_t>(lv, inv, og, y, st);
+}
+
+hipError_t launch_scatter_bwd(const Levels& lv, int32_t in_f32, const int32_t* gmap,
+                              const float* og, const void* dy, void* dog, void* dogt,
+                              float* delta, hipStream_t st) {
+  return in_f32 ? scatter_bwd_t<float>(lv, gmap, og, dy, dog, dogt, delta, st)
+                : scatter_bwd_t<uint16_t>(lv, gmap, og, dy, dog, dogt, delta, st);
+}
+
+hipError_t launch_gather_pool_bwd(const Levels& lv, int32_t out_f32, const int32_t* inv,
+                                  const float* dqg, const float* dkg, const float* dvg,
+                                  void* dq, void* dk, void* dv, hipStream_t st) {
+  return out_f32 ? gpb_t<float>(lv, inv, dqg, dkg, dvg, dq, dk, dv, st)
+                 : gpb_t<uint16_t>(lv, inv, dqg, dkg, dvg, dq, dk, dv, st);
+}
+
+}  // namespace lh

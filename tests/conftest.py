@@ -16,3 +16,11 @@ def pytest_configure(config):
 def rng():
     import numpy as np
     return np.random.default_rng(12345)
+
+
+def pytest_sessionstart(session):
+    """Build liblh.so in-tree when nothing is built yet (a built library is used as is)."""
+    from hierarchical_sparse_attention_lh_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from hierarchical_sparse_attention_lh_amd import build
+        build.build()
