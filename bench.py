@@ -63,6 +63,31 @@ def algorithmic(w, info):
     return by, fl
 
 
+KERNEL_OF_STAGE = {"attn_fwd": "attn_fwd_kernel<{d}>", "attn_bwd_dkdv": "attn_bwd_kv_kernel<{d}>",
+                   "attn_bwd_dq": "attn_bwd_q_kernel<{d}>"}
+
+
+def measured_traffic(workload, stage, head_dim):
+    """HBM bytes per launch of a stage's kernel from the committed rocprofv3 counter runs,
+    or None when there are none or the kernel sources changed since they were taken."""
+    import glob
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"{workload}_counters.json")
+    if not os.path.exists(path) or stage not in KERNEL_OF_STAGE:
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for src in sorted(glob.glob(os.path.join(ROOT, "hierarchical_sparse_attention_lh_amd", "csrc", "*"))):
+        with open(src, "rb") as f:
+            h.update(f.read())
+    if h.hexdigest()[:16] != rec.get("csrc_sha256_16"):
+        return None
+    t = rec["per_launch"].get(KERNEL_OF_STAGE[stage].format(d=head_dim))
+    return None if t is None else int(t["read_bytes"] + t["write_bytes"])
+
+
 def time_staged(layer, steps, warmup, torch):
     names = [n for n, _ in layer.stages_fwd + layer.stages_bwd]
     stages = layer.stages_fwd + layer.stages_bwd
@@ -143,6 +168,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention baseline")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this "
@@ -153,6 +180,14 @@ def main():
     import torch
 
     from hierarchical_sparse_attention_lh_amd import _lib, ops, synth
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
+        del src, dst
 
     w = synth.WORKLOADS[args.workload]
     log(f"workload {w}")
@@ -196,7 +231,8 @@ def main():
         ach = fl[dom] / (per[dom] * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(w.name, dom, w.head_dim),
                 "avg_ms": round(per[dom], 4)}
     else:
         ach = by[dom] / (per[dom] * 1e-3) / 1e9
