@@ -381,13 +381,18 @@ def head_selection(k: np.ndarray, cfg: Config, sizes=None):
     return k_levels, scores, sel
 
 
-def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, cfg: Config) -> tuple:
-    """Forward of one (batch, head); q, k, v are [N, D]. Returns (Y [N, D], HeadState)."""
+def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, cfg: Config, sel=None) -> tuple:
+    """Forward of one (batch, head); q, k, v are [N, D]. Returns (Y [N, D], HeadState).
+
+    `sel` (optional, {level: ascending kept indices}) replaces the top-K step's result, so
+    the remaining steps can be checked on a selection made elsewhere.
+    """
     n, d = q.shape
     sizes = level_sizes(n, cfg.levels, cfg.pool)
     q_levels = pool_pyramid(q, cfg.levels, cfg.pool)
     v_levels = pool_pyramid(v, cfg.levels, cfg.pool)
-    k_levels, scores, sel = head_selection(k, cfg, sizes)
+    k_levels, scores, own_sel = head_selection(k, cfg, sizes)
+    sel = own_sel if sel is None else {lv: np.asarray(sel[lv], np.int64) for lv in own_sel}
     glev, gidx = gathered_set(sel, sizes, cfg)
     inv = inverse_map(glev, gidx, sizes)
     rnd = round_bf16 if cfg.bf16_attention else (lambda a: a)

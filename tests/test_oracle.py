@@ -439,3 +439,17 @@ def test_direct_mode_length():
     cfg = _cfg(3, 4, 128, 64, mode=O.DIRECT)
     sizes, sel, glev, gidx = _random_state(4096, cfg)
     assert len(glev) == 256 + 128 + 128 == O.gathered_length(4096, cfg)
+
+
+def test_given_selection_reproduces_own_selection(rng):
+    n, h, d = 1024, 1, 8
+    cfg = _cfg(3, 4, 24, 16, bf16=False)
+    x = {w: rng.standard_normal((n, d)) for w in "qkv"}
+    y0, st0 = O.head_forward(x["q"], x["k"], x["v"], cfg)
+    y1, st1 = O.head_forward(x["q"], x["k"], x["v"], cfg, sel=st0.sel)
+    assert np.array_equal(y0, y1)
+    # a different (valid) selection changes the gathered set but keeps its length
+    other = {lv: np.sort(np.random.default_rng(1).permutation(len(st0.scores[lv]))[:len(s)])
+             for lv, s in st0.sel.items()}
+    y2, st2 = O.head_forward(x["q"], x["k"], x["v"], cfg, sel=other)
+    assert len(st2.glev) == len(st0.glev) and not np.array_equal(y2, y0)
