@@ -13,14 +13,20 @@
 //     lane owns one query (C column) and 32 of the tile's 64 keys: the running max and sum
 //     are per-lane scalars, combined with the partner lane (l ^ 32) by one cross-lane swap.
 //   * O^T = V^T P^T: P leaves the C registers as a bf16 hi/lo pair (two MFMAs, ~16-bit
-//     probabilities) and is the B operand directly (the k order inside an instruction is
-//     permuted identically on the V^T side, so P never touches LDS).  V^T comes
-//     pre-transposed from the gather stage, so both A operands are plain 16-byte /
-//     2 x 8-byte LDS reads.
-//   * K and V^T tiles are double-buffered in LDS; the next tile's global loads are in flight
-//     while the current tile is multiplied.
-//   * Workgroups are mapped XCD-aware (one contiguous range of heads per XCD) and heavy
+//     probabilities) and is the B operand directly; V^T is stored with the k order of that
+//     operand (swap23 layout), so each A operand is one 16-byte LDS read and P never
+//     touches LDS.
+//   * K and V^T tiles are staged with direct global->LDS loads into XOR-swizzled LDS rows,
+//     double-buffered: the next tile is in flight while the current one is multiplied.
+//   * Only diagonal and ragged-tail tiles evaluate the causal mask.  The running max moves
+//     only when a row's maximum grows by more than 8 (base 2), so most tiles skip the
+//     rescale of the accumulators; the final division by the row sum is exact either way.
+//   * The row sum is a per-tile tree sum added to a Kahan-compensated total: thousands of
+//     small terms otherwise drift by ~1e-4 relative, which the backward's Delta amplifies.
+//   * Workgroups are mapped XCD-aware (one contiguous range of heads per XCD), heavy
 //     (diagonal-far) query tiles first.
+#include <type_traits>
+
 #include "lh_internal.h"
 #include "lh_mfma.h"
 
@@ -29,121 +35,92 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kSlack = 8.0f;  // base-2 growth of the row max tolerated before a rescale
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                        const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ vt,
                                                        float* __restrict__ o,
-                                                       float* __restrict__ lse, int64_t S,
-                                                       int64_t Sp, int64_t BH, float sl2) {
+                                                       float* __restrict__ lse, int S, int Sp,
+                                                       int64_t BH, float sl2) {
   constexpr int BM = 128, BN = 64;
-  constexpr int KR = D + 8;   // K tile row stride in LDS (elements)
-  constexpr int VR = BN + 8;  // V^T tile row stride in LDS
-  constexpr int KG = D / 8, KPER = BN * KG / 256;
-  constexpr int VG = BN / 8, VPER = D * VG / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BN * KR];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][D * VR];
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][D * BN];
 
-  const int64_t nqt = Sp / BM;
+  const int nqt = Sp / BM;
   const int64_t item = xcd_item(blockIdx.x, BH * nqt);
   const int64_t bh = item / nqt;
-  const int64_t qt = nqt - 1 - item % nqt;
+  const int qt = nqt - 1 - static_cast<int>(item % nqt);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, lq = lane & 31;
-  const int64_t qw = qt * BM + wave * 32;
-  const int64_t myq = qw + lq;
+  const int q0 = qt * BM;
+  const int qw = q0 + wave * 32;
+  const int myq = qw + lq;
 
-  const uint16_t* qb = q + bh * Sp * D;
   const uint16_t* kb = k + bh * Sp * D;
   const uint16_t* vb = vt + bh * D * Sp;
 
   bf16x8 qreg[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = ld_op16(qb + myq * D + 16 * kk + hl * 8);
+  for (int kk = 0; kk < D / 16; ++kk)
+    qreg[kk] = ld_op16(q + (bh * Sp + myq) * D + 16 * kk + hl * 8);
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
-  // running max (base-2 units) and the row sum; the sum is Kahan-compensated because
-  // thousands of small probabilities are added to it (plain float32 summation drifts by
-  // ~1e-4 relative at S ~ 1e4, which the backward's Delta = rowsum(dO * O) amplifies)
   float m_run = -INFINITY, l_run = 0.f, l_cmp = 0.f;
 
-  const int64_t kend = S < (qt + 1) * BM ? S : (qt + 1) * BM;
-  const int nkt = static_cast<int>((kend + BN - 1) / BN);
+  const int kend = S < q0 + BM ? S : q0 + BM;
+  const int nkt = (kend + BN - 1) / BN;
 
-  u32x4 kreg[KPER], vreg[VPER];
-  auto gload = [&](int kt) {
-    const int64_t k0 = static_cast<int64_t>(kt) * BN;
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int idx = tid + 256 * i, r = idx / KG, c = idx % KG;
-      kreg[i] = *reinterpret_cast<const u32x4*>(kb + (k0 + r) * D + c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VPER; ++i) {
-      const int idx = tid + 256 * i, r = idx / VG, c = idx % VG;
-      vreg[i] = *reinterpret_cast<const u32x4*>(vb + r * Sp + k0 + c * 8);
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int idx = tid + 256 * i, r = idx / KG, c = idx % KG;
-      *reinterpret_cast<u32x4*>(&ks[buf][r * KR + c * 8]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPER; ++i) {
-      const int idx = tid + 256 * i, r = idx / VG, c = idx % VG;
-      *reinterpret_cast<u32x4*>(&vs[buf][r * VR + c * 8]) = vreg[i];
-    }
+  auto stage = [&](int t, int buf) {
+    stage_tile<BN, D, 256>(kb + static_cast<int64_t>(t) * BN * D, D, ks[buf], tid);
+    stage_tile<D, BN, 256>(vb + t * BN, Sp, vs[buf], tid);
   };
 
-  gload(0);
-  swrite(0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
-
+  auto tile = [&](auto masked, int t, int buf) {
     f32x16 sacc[2];
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) {
       sacc[b2] = zero16();
-      const uint16_t* ka = &ks[buf][(b2 * 32 + lq) * KR + hl * 8];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) sacc[b2] = mfma32(ld_op16(ka + 16 * kk), qreg[kk], sacc[b2]);
+      for (int kk = 0; kk < D / 16; ++kk)
+        sacc[b2] = mfma32(lds_op<D>(ks[buf], b2 * 32 + lq, 2 * kk + hl), qreg[kk], sacc[b2]);
     }
-
-    const int64_t k0 = static_cast<int64_t>(kt) * BN;
-    if (k0 + BN - 1 > qw || k0 + BN > S) {
+    if constexpr (decltype(masked)::value) {
+      const int k0 = t * BN;
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t key = k0 + b2 * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+          const int key = k0 + b2 * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
           if (key > myq || key >= S) sacc[b2][r] = -INFINITY;
         }
     }
-
     float mx = sacc[0][0];
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[b2][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * sl2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    const bool grow = mx > m_run + kSlack;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      l_run *= alpha;
+      l_cmp *= alpha;
+      m_run = m_new;
+    }
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[b2][r] = __builtin_amdgcn_exp2f(fmaf(sacc[b2][r], sl2, -m_new));
+      for (int r = 0; r < 16; ++r)
+        sacc[b2][r] = __builtin_amdgcn_exp2f(fmaf(sacc[b2][r], sl2, -m_run));
     float part[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) part[r] = sacc[0][r] + sacc[1][r];
@@ -151,29 +128,35 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restric
     for (int w2 = 8; w2 >= 1; w2 >>= 1)
 #pragma unroll
       for (int r = 0; r < w2; ++r) part[r] += part[r + w2];
-    {
-      l_run *= alpha;
-      l_cmp *= alpha;
-      const float yk = part[0] - l_cmp;
-      const float tk = l_run + yk;
-      l_cmp = (tk - l_run) - yk;
-      l_run = tk;
-    }
-
+    const float yk = part[0] - l_cmp;
+    const float tk = l_run + yk;
+    l_cmp = (tk - l_run) - yk;
+    l_run = tk;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t4 = 0; t4 < 4; ++t4) {
       bf16x8 ph, pl;
-      c_to_op2(sacc[t >> 1], t & 1, ph, pl);
+      c_to_op2(sacc[t4 >> 1], t4 & 1, ph, pl);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const uint16_t* va = &vs[buf][(db * 32 + lq) * VR + 16 * t + hl * 4];
-        const bf16x8 a = ld_op8x2(va, va + 8);
+        const bf16x8 a = lds_op<BN>(vs[buf], db * 32 + lq, 2 * t4 + hl);
         oacc[db] = mfma32(a, pl, oacc[db]);
         oacc[db] = mfma32(a, ph, oacc[db]);
       }
     }
+  };
 
-    if (kt + 1 < nkt) swrite(buf ^ 1);
+  stage(0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int t = 0; t < nkt; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nkt) stage(t + 1, buf ^ 1);
+    const int k0 = t * BN;
+    if (k0 + BN - 1 > qw || k0 + BN > S)
+      tile(std::true_type{}, t, buf);
+    else
+      tile(std::false_type{}, t, buf);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -204,12 +187,13 @@ hipError_t launch_attn_fwd(int64_t B, int64_t H, int64_t S, int32_t D, float sca
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   const auto* vv = static_cast<const uint16_t*>(vt);
+  const int s32 = static_cast<int>(S), sp32 = static_cast<int>(Sp);
   if (D == 64)
     hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(blocks), dim3(256), 0, st, qq, kk, vv, o, lse,
-                       S, Sp, BH, sl2);
+                       s32, sp32, BH, sl2);
   else
     hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(blocks), dim3(256), 0, st, qq, kk, vv, o,
-                       lse, S, Sp, BH, sl2);
+                       lse, s32, sp32, BH, sl2);
   return hipGetLastError();
 }
 

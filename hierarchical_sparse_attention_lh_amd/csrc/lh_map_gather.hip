@@ -21,8 +21,10 @@
 //
 // Gather design: one workgroup per 64 slots of one head.  Rows are copied with 16-byte
 // vectors into the row layout and staged in LDS to write the transposed layout with
-// 16-byte stores as well.  Padding slots S..Sp-1 are written as zeros.
+// 16-byte stores as well; the transposed layout stores slot s at column swap23(s), the
+// order in which the attention kernels consume it.  Padding slots S..Sp-1 are zeros.
 #include "lh_internal.h"
+#include "lh_mfma.h"
 
 namespace lh {
 namespace {
@@ -184,8 +186,8 @@ __global__ __launch_bounds__(256) void gather_kernel(
         uint32_t pk[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          pk[u] = static_cast<uint32_t>(tile[(sg + 2 * u) * LROW + d]) |
-                  (static_cast<uint32_t>(tile[(sg + 2 * u + 1) * LROW + d]) << 16);
+          pk[u] = static_cast<uint32_t>(tile[swap23(sg + 2 * u) * LROW + d]) |
+                  (static_cast<uint32_t>(tile[swap23(sg + 2 * u + 1) * LROW + d]) << 16);
         *reinterpret_cast<uint4*>(to + (bh * D + d) * Sp + s0 + sg) =
             make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }

@@ -89,6 +89,56 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// ------------------------------------------------------------------------------------------
+// Operand-friendly layouts.
+//
+// Transposed tensors ([.., D, Sp]) store sequence position s at column swap23(s): bits 2 and 3
+// of s exchanged (an involution).  Within each group of 16 the stored order is
+// 0-3, 8-11, 4-7, 12-15, which is exactly the k order in which a C tile leaves an MFMA as the
+// next product's B operand (see c_to_op): the matching A operand of lane l is then the single
+// 16-byte chunk 2*t + (l/32) of the row instead of two 8-byte pieces.
+__host__ __device__ __forceinline__ int64_t swap23(int64_t s) {
+  return (s & ~int64_t(12)) | ((s & 4) << 1) | ((s & 8) >> 1);
+}
+
+// LDS tiles are unpadded rows whose 16-byte chunks are XOR-swizzled with (row & 7): eight
+// consecutive rows read at one logical chunk index touch eight different bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+// 16-byte MFMA operand: logical chunk `chunk` of `row` in a swizzled LDS tile.
+template <int ROW_ELEMS>
+__device__ __forceinline__ bf16x8 lds_op(const uint16_t* tile, int row, int chunk) {
+  return ld_op16(tile + row * ROW_ELEMS + (swz(row, chunk) << 3));
+}
+
+// Stage ROWS x ROW_ELEMS bf16 (row stride `gstride` elements in global memory) into a swizzled
+// LDS tile with gfx950 direct global->LDS loads: each wave instruction moves 64 x 16 bytes into
+// 1 KB of contiguous LDS, so lane l fetches the global chunk that belongs at LDS chunk
+// (instruction base + l).  No VGPRs hold the data; completion is tracked by vmcnt.
+template <int ROWS, int ROW_ELEMS, int NT>
+__device__ __forceinline__ void stage_tile(const uint16_t* g, int64_t gstride, uint16_t* lds,
+                                           int tid) {
+  constexpr int CPR = ROW_ELEMS / 8;        // 16-byte chunks per row
+  constexpr int CHUNKS = ROWS * CPR;
+  static_assert(CHUNKS % NT == 0, "tile must be a whole number of 16-byte loads per thread");
+  const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int i = 0; i < CHUNKS / NT; ++i) {
+    const int base = (i * (NT / 64) + wave) * 64;  // first LDS chunk of this wave instruction
+    const int lin = base + lane;
+    const int row = lin / CPR, pc = lin % CPR;
+    const int c = pc ^ (row & 7);
+    __builtin_amdgcn_global_load_lds(g + row * gstride + c * 8, lds + base * 8, 16, 0, 0);
+  }
+}
+
+// 64 floats into LDS with one wave instruction (4 bytes per lane).
+__device__ __forceinline__ void stage_f32x64(const float* g, float* lds, int lane) {
+  __builtin_amdgcn_global_load_lds(g + lane, lds, 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Map a linear block id to a work item so that each of the 8 XCDs (workgroups are handed
 // to XCDs round-robin) receives one contiguous range of items; items of one head then run
 // on one XCD and share its L2.

@@ -20,6 +20,7 @@
 // once to bf16, writes the row layout directly and the transposed layout through LDS, and
 // fuses Delta = rowsum(dO * O) for the attention backward.
 #include "lh_internal.h"
+#include "lh_mfma.h"
 
 namespace lh {
 namespace {
@@ -150,8 +151,8 @@ __global__ __launch_bounds__(256) void scatter_bwd_kernel(
     uint32_t pk[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      pk[u] = static_cast<uint32_t>(tile[(sg + 2 * u) * LR + d]) |
-              (static_cast<uint32_t>(tile[(sg + 2 * u + 1) * LR + d]) << 16);
+      pk[u] = static_cast<uint32_t>(tile[swap23(sg + 2 * u) * LR + d]) |
+              (static_cast<uint32_t>(tile[swap23(sg + 2 * u + 1) * LR + d]) << 16);
     *reinterpret_cast<uint4*>(dogt + (bh * D + d) * Sp + s0 + sg) =
         make_uint4(pk[0], pk[1], pk[2], pk[3]);
   }

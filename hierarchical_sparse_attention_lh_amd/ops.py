@@ -124,6 +124,23 @@ def lh_gather(cfg, q, k, v, pq, pk, pv, gmap, with_backward=True):
     return out
 
 
+def swap23_index(n: int, device=None):
+    """Column order of the library's transposed tensors: slot s sits at column swap23(s)
+    (bits 2 and 3 of s exchanged; an involution, so the same index maps both ways)."""
+    s = torch.arange(n, device=device)
+    return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1)
+
+
+def to_transposed(x):
+    """[..., Sp, D] -> [..., D, Sp] in the library's transposed layout (Sp a multiple of 16)."""
+    return x.transpose(-1, -2)[..., swap23_index(x.shape[-2], x.device)].contiguous()
+
+
+def from_transposed(xt):
+    """Inverse of to_transposed."""
+    return xt[..., swap23_index(xt.shape[-1], xt.device)].transpose(-1, -2).contiguous()
+
+
 def attn_desc(batch, heads, seq, head_dim, scale=0.0) -> LhAttnDesc:
     return LhAttnDesc(batch, heads, seq, head_dim, scale)
 

@@ -51,7 +51,10 @@
  *     different buffers may run concurrently; the library has no mutable global state.
  *   - Tensors are dense and row-major.  Token tensors are [B, N, H, D].  Gathered-domain
  *     tensors store Sp = S rounded up to a multiple of 128 slots: rows [B, H, Sp, D],
- *     "transposed" [B, H, D, Sp], per-slot vectors [B, H, Sp].  Slots S..Sp-1 are padding;
+ *     "transposed" [B, H, D, Sp], per-slot vectors [B, H, Sp].  In a transposed tensor,
+ *     slot s sits at column swap23(s) = s with its bits 2 and 3 exchanged (within every
+ *     group of 16 slots the stored order is 0-3, 8-11, 4-7, 12-15), the k order the MFMA
+ *     operands consume.  Slots S..Sp-1 are padding;
  *     the library writes them as finite values (zeros), and callers of the attention entry
  *     points must do the same.
  *   - The forward and backward are deterministic (no atomics, fixed reduction orders).

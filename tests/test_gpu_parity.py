@@ -194,7 +194,7 @@ def test_map_and_gather(w):
                             rows.append(pooled[name][b, info.pooled_offset[lv] + j, h])
                     want = O.round_bf16(np.stack(rows))
                     got = f64(g[name][b, h, :S])
-                    got_t = f64(g[name + "t"][b, h, :, :S]).T
+                    got_t = f64(ops.from_transposed(g[name + "t"])[b, h, :S])
                     assert np.array_equal(got, got_t)
                     diff = got != want
                     near += int(diff.sum())
@@ -202,7 +202,7 @@ def test_map_and_gather(w):
                         step = np.abs(want[diff]) * 2.0**-7
                         assert np.all(np.abs(got[diff] - want[diff]) <= step * 1.001)
                     assert np.all(f64(g[name][b, h, S:]) == 0)
-                    assert np.all(f64(g[name + "t"][b, h, :, S:]) == 0)
+                    assert np.all(f64(ops.from_transposed(g[name + "t"])[b, h, S:]) == 0)
     print(f"[{w.name}] gathered elements one bf16 step off (ties): {near}")
     assert near <= 3
 
@@ -225,7 +225,7 @@ def _attn_case(seq, d, heads=2, seed=0):
 def test_attention_forward(seq, d):
     x, sp = _attn_case(seq, d, seed=seq + d)
     q, k, v = (x[n].to(DEV) for n in "qkv")
-    vt = v.transpose(2, 3).contiguous()
+    vt = ops.to_transposed(v)
     desc = ops.attn_desc(1, 2, seq, d)
     o, lse = ops.lh_attn_fwd(desc, q, k, vt)
     torch.cuda.synchronize()
@@ -252,11 +252,10 @@ def test_attention_backward(seq, d):
     dout = torch.from_numpy(dout_np).to(torch.bfloat16)
     q, k, v, do = (t.to(DEV) for t in (x["q"], x["k"], x["v"], dout))
     desc = ops.attn_desc(1, 2, seq, d)
-    o, lse = ops.lh_attn_fwd(desc, q, k, v.transpose(2, 3).contiguous())
+    o, lse = ops.lh_attn_fwd(desc, q, k, ops.to_transposed(v))
     delta = (do.float() * o).sum(-1)
-    dq, dk, dv = ops.lh_attn_bwd(desc, q, k, v, q.transpose(2, 3).contiguous(),
-                                 k.transpose(2, 3).contiguous(), lse, delta, do,
-                                 do.transpose(2, 3).contiguous())
+    dq, dk, dv = ops.lh_attn_bwd(desc, q, k, v, ops.to_transposed(q), ops.to_transposed(k), lse,
+                                 delta, do, ops.to_transposed(do))
     torch.cuda.synchronize()
     for h in range(2):
         qq, kk, vv, dd = (f64(t[0, h, :seq]) for t in (x["q"], x["k"], x["v"], dout))
@@ -315,8 +314,9 @@ def test_scatter_and_adjoints(w):
                 mag = O.scatter_backward(np.abs(x["dy"][b, :, h].astype(np.float64)), glev, gidx, w.pool)
                 step = 2.0**-7 * np.maximum(np.abs(gd), np.abs(rdog))
                 assert np.all(np.abs(gd - rdog) <= step + 64 * 2.0**-24 * mag)
-            assert np.array_equal(f64(dogt[b, h, :, :S]).T, gd)
-            assert np.all(f64(dog[b, h, S:]) == 0) and np.all(f64(dogt[b, h, :, S:]) == 0)
+            assert np.array_equal(f64(ops.from_transposed(dogt)[b, h, :S]), gd)
+            assert np.all(f64(dog[b, h, S:]) == 0)
+            assert np.all(f64(ops.from_transposed(dogt)[b, h, S:]) == 0)
             rdelta = np.sum(gd * og_np[b, h, :S], axis=1)  # Delta of the GPU's own dOg
             assert np.allclose(f64(delta[b, h, :S]), rdelta, rtol=1e-5, atol=1e-5)
             assert np.all(f64(delta[b, h, S:]) == 0)
