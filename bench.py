@@ -63,8 +63,8 @@ def algorithmic(w, info):
     return by, fl
 
 
-KERNEL_OF_STAGE = {"attn_fwd": "attn_fwd_kernel<{d}>", "attn_bwd_dkdv": "attn_bwd_kv_kernel<{d}>",
-                   "attn_bwd_dq": "attn_bwd_q_kernel<{d}>"}
+KERNEL_OF_STAGE = {"attn_fwd": "attn_fwd_d{d}", "attn_bwd_dkdv": "attn_bwd_kv_d{d}",
+                   "attn_bwd_dq": "attn_bwd_q_d{d}"}
 
 
 def measured_traffic(workload, stage, head_dim):

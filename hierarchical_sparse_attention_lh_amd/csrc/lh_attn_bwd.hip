@@ -34,7 +34,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------- key pass
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_kv_kernel(
+__device__ __forceinline__ void attn_bwd_kv_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ qt,
     const float* __restrict__ lse, const float* __restrict__ delta,
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_kernel(
 
 // -------------------------------------------------------------------------- query pass
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_q_kernel(
+__device__ __forceinline__ void attn_bwd_q_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ kt,
     const float* __restrict__ lse, const float* __restrict__ delta,
@@ -290,6 +290,40 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(
     }
 }
 
+
+// D = 64 fits two waves per SIMD in both passes (no AGPR shuffling, no spills); D = 128
+// keeps the compiler's default.
+#define LH_KV_ARGS                                                                          \
+  const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,                          \
+      const uint16_t *__restrict__ v, const uint16_t *__restrict__ qt,                     \
+      const float *__restrict__ lse, const float *__restrict__ delta,                      \
+      const uint16_t *__restrict__ dout, const uint16_t *__restrict__ doutt,               \
+      float *__restrict__ dk, float *__restrict__ dv, int S, int Sp, int64_t BH,           \
+      float scale, float sl2
+#define LH_Q_ARGS                                                                           \
+  const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,                          \
+      const uint16_t *__restrict__ v, const uint16_t *__restrict__ kt,                     \
+      const float *__restrict__ lse, const float *__restrict__ delta,                      \
+      const uint16_t *__restrict__ dout, float *__restrict__ dq, int S, int Sp, int64_t BH, \
+      float scale, float sl2
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+attn_bwd_kv_d64(LH_KV_ARGS) {
+  attn_bwd_kv_body<64>(q, k, v, qt, lse, delta, dout, doutt, dk, dv, S, Sp, BH, scale, sl2);
+}
+__global__ __launch_bounds__(256) void attn_bwd_kv_d128(LH_KV_ARGS) {
+  attn_bwd_kv_body<128>(q, k, v, qt, lse, delta, dout, doutt, dk, dv, S, Sp, BH, scale, sl2);
+}
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+attn_bwd_q_d64(LH_Q_ARGS) {
+  attn_bwd_q_body<64>(q, k, v, kt, lse, delta, dout, dq, S, Sp, BH, scale, sl2);
+}
+__global__ __launch_bounds__(256) void attn_bwd_q_d128(LH_Q_ARGS) {
+  attn_bwd_q_body<128>(q, k, v, kt, lse, delta, dout, dq, S, Sp, BH, scale, sl2);
+}
+#undef LH_KV_ARGS
+#undef LH_Q_ARGS
+
 }  // namespace
 
 hipError_t launch_attn_bwd_pass(int pass, int64_t B, int64_t H, int64_t S, int32_t D,
@@ -311,20 +345,20 @@ hipError_t launch_attn_bwd_pass(int pass, int64_t B, int64_t H, int64_t S, int32
   const int s32 = static_cast<int>(S), sp32 = static_cast<int>(Sp);
   if (pass & 1) {
     if (D == 64)
-      hipLaunchKernelGGL(attn_bwd_kv_kernel<64>, dim3(blocks), dim3(256), 0, st, Q, K, V, QT,
+      hipLaunchKernelGGL(attn_bwd_kv_d64, dim3(blocks), dim3(256), 0, st, Q, K, V, QT,
                          lse, delta, DO, DOT, dk, dv, s32, sp32, BH, scale, sl2);
     else
-      hipLaunchKernelGGL(attn_bwd_kv_kernel<128>, dim3(blocks), dim3(256), 0, st, Q, K, V, QT,
+      hipLaunchKernelGGL(attn_bwd_kv_d128, dim3(blocks), dim3(256), 0, st, Q, K, V, QT,
                          lse, delta, DO, DOT, dk, dv, s32, sp32, BH, scale, sl2);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (pass & 2) {
     if (D == 64)
-      hipLaunchKernelGGL(attn_bwd_q_kernel<64>, dim3(blocks), dim3(256), 0, st, Q, K, V, KT,
+      hipLaunchKernelGGL(attn_bwd_q_d64, dim3(blocks), dim3(256), 0, st, Q, K, V, KT,
                          lse, delta, DO, dq, s32, sp32, BH, scale, sl2);
     else
-      hipLaunchKernelGGL(attn_bwd_q_kernel<128>, dim3(blocks), dim3(256), 0, st, Q, K, V, KT,
+      hipLaunchKernelGGL(attn_bwd_q_d128, dim3(blocks), dim3(256), 0, st, Q, K, V, KT,
                          lse, delta, DO, dq, s32, sp32, BH, scale, sl2);
   }
   return hipGetLastError();

@@ -38,12 +38,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;  // base-2 growth of the row max tolerated before a rescale
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restrict__ q,
-                                                       const uint16_t* __restrict__ k,
-                                                       const uint16_t* __restrict__ vt,
-                                                       float* __restrict__ o,
-                                                       float* __restrict__ lse, int S, int Sp,
-                                                       int64_t BH, float sl2) {
+__device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
+                                              const uint16_t* __restrict__ k,
+                                              const uint16_t* __restrict__ vt,
+                                              float* __restrict__ o, float* __restrict__ lse,
+                                              int S, int Sp, int64_t BH, float sl2) {
   constexpr int BM = 128, BN = 64;
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t vs[2][D * BN];
@@ -175,6 +174,24 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restric
   if (hl == 0) lse[bh * Sp + myq] = m_run * kLn2 + __logf(l_tot);
 }
 
+// D = 64 fits three waves per SIMD (134 VGPRs), so MFMA work of one wave overlaps the
+// softmax arithmetic of the others; D = 128 keeps the compiler's default.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void
+attn_fwd_d64(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+             const uint16_t* __restrict__ vt, float* __restrict__ o, float* __restrict__ lse,
+             int S, int Sp, int64_t BH, float sl2) {
+  attn_fwd_body<64>(q, k, vt, o, lse, S, Sp, BH, sl2);
+}
+
+__global__ __launch_bounds__(256) void attn_fwd_d128(const uint16_t* __restrict__ q,
+                                                     const uint16_t* __restrict__ k,
+                                                     const uint16_t* __restrict__ vt,
+                                                     float* __restrict__ o,
+                                                     float* __restrict__ lse, int S, int Sp,
+                                                     int64_t BH, float sl2) {
+  attn_fwd_body<128>(q, k, vt, o, lse, S, Sp, BH, sl2);
+}
+
 }  // namespace
 
 hipError_t launch_attn_fwd(int64_t B, int64_t H, int64_t S, int32_t D, float scale,
@@ -189,10 +206,10 @@ hipError_t launch_attn_fwd(int64_t B, int64_t H, int64_t S, int32_t D, float sca
   const auto* vv = static_cast<const uint16_t*>(vt);
   const int s32 = static_cast<int>(S), sp32 = static_cast<int>(Sp);
   if (D == 64)
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(blocks), dim3(256), 0, st, qq, kk, vv, o, lse,
+    hipLaunchKernelGGL(attn_fwd_d64, dim3(blocks), dim3(256), 0, st, qq, kk, vv, o, lse,
                        s32, sp32, BH, sl2);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(blocks), dim3(256), 0, st, qq, kk, vv, o,
+    hipLaunchKernelGGL(attn_fwd_d128, dim3(blocks), dim3(256), 0, st, qq, kk, vv, o,
                        lse, s32, sp32, BH, sl2);
   return hipGetLastError();
 }
