@@ -69,6 +69,10 @@ lh_status check_config(const lh_config* c, Levels* lv) {
     if (pw > kMaxTokens) return LH_ERR_SHAPE;
   }
   if (L.N % L.pw[L.L - 1] != 0) return LH_ERR_SHAPE;
+  const bool pow2 = (L.p & (L.p - 1)) == 0;
+  int lgp = 0;
+  while ((1 << lgp) < L.p) ++lgp;
+  for (int l = 0; l < LH_MAX_LEVELS; ++l) L.lg[l] = pow2 ? l * lgp : -1;
   int64_t off = 0, poff = 0;
   for (int l = 0; l < L.L; ++l) {
     L.n[l] = L.N / L.pw[l];

@@ -27,7 +27,13 @@ struct Levels {
   int64_t P1;                   // pooled rows (levels >= 1)
   int64_t K;                    // sel_total
   int64_t S;                    // gathered length
+  int32_t lg[LH_MAX_LEVELS];    // log2(p^l) when p is a power of two, else -1
 };
+
+// floor(x / p^l) for non-negative x < 2^31, by a shift when p is a power of two.
+__host__ __device__ __forceinline__ int level_div(const Levels& lv, int l, int x) {
+  return lv.lg[l] >= 0 ? (x >> lv.lg[l]) : x / static_cast<int>(lv.pw[l]);
+}
 
 // ---------------------------------------------------------------- bf16 helpers
 // bfloat16 values are carried as raw 16-bit patterns.

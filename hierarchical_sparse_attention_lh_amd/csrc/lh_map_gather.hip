@@ -136,10 +136,11 @@ __global__ __launch_bounds__(256) void gather_kernel(
   __shared__ uint16_t tile[TS * LROW];
   __shared__ int32_t ids[TS];
 
-  const int64_t bh = blockIdx.y;
+  const int64_t BH = lv.B * lv.H;
+  const int64_t bh = blockIdx.x % BH;  // heads fastest: the heads' slices of a row together
   const int64_t b = bh / lv.H;
   const int64_t h = bh % lv.H;
-  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * TS;
+  const int64_t s0 = static_cast<int64_t>(blockIdx.x / BH) * TS;
   const int tid = threadIdx.x;
   if (tid < TS) {
     const int64_t s = s0 + tid;
@@ -200,7 +201,7 @@ template <int D, typename Tin, typename Tpool>
 hipError_t gather_dispatch(const Levels& lv, int64_t Sp, const void* const x[3],
                            const void* const px[3], const int32_t* gmap, void* const rows[3],
                            void* const trans[3], hipStream_t st) {
-  dim3 grid(static_cast<unsigned>(Sp / 64), static_cast<unsigned>(lv.B * lv.H));
+  dim3 grid(static_cast<unsigned>(Sp / 64 * lv.B * lv.H));
   hipLaunchKernelGGL((gather_kernel<D, Tin, Tpool>), grid, dim3(256), 0, st, lv, Sp,
                      static_cast<const Tin*>(x[0]), static_cast<const Tin*>(x[1]),
                      static_cast<const Tin*>(x[2]), static_cast<const Tpool*>(px[0]),

@@ -13,12 +13,13 @@
 // of a gathered pooled entry 1/p^l of its gradient.
 //
 // Design: all three kernels are pull-based (each output element is written by exactly one
-// thread, no atomics) and HBM-bound.  A workgroup owns 32 consecutive tokens (or slots) of
-// one head; D/8 lanes per row each move 8 columns with 16-/32-byte vectors.  Per token the
-// L level lookups go through `inv` ([B, H, P]); coarse entries repeat across neighbouring
-// tokens and hit in cache.  Scatter backward sums each slot's token span in float32, rounds
-// once to bf16, writes the row layout directly and the transposed layout through LDS, and
-// fuses Delta = rowsum(dO * O) for the attention backward.
+// thread, no atomics) and HBM-bound.  Scatter and gather+pool backward walk tokens: a
+// thread owns 8 columns of the full token row and a run of 64 tokens, keeping every coarse
+// level's current contribution in registers (reloaded only when that level's entry
+// changes), so token rows are written whole and coarse rows are read once per run.
+// Scatter backward owns 64 slots of one head, sums each slot's token span in float32,
+// rounds once to bf16, writes the row layout directly and the transposed layout through
+// LDS, and fuses Delta = rowsum(dO * O) for the attention backward.
 #include "lh_internal.h"
 #include "lh_mfma.h"
 
@@ -59,37 +60,101 @@ __device__ __forceinline__ void st8(uint16_t* p, const float (&v)[8]) {
 constexpr int kTok = 32;  // tokens (or slots) per workgroup
 
 // ----------------------------------------------------------------------------- scatter
-template <int D, typename Tout>
+// Token-walking layout shared by scatter and gather+pool backward: a thread owns 8 columns
+// of the full token row (all heads side by side, so a wave writes 1 KB contiguous) and walks
+// a run of kRun tokens in batches of 8.  Per batch it first loads every `inv` slot the batch
+// needs -- level 0 for each token, and for each coarser level the few entries the batch
+// touches -- as independent loads; then the rows of gathered entries, each coarse row once
+// per entry (it stays in registers while the entry lasts).  Level-0 rows are loaded only for
+// the few tokens that are gathered themselves.
+constexpr int kRun = 64;
+constexpr int kPre = 6;  // entries of one level a batch of 8 tokens can touch (p >= 2)
+
+// OFFSET = 1: token t takes entry floor((t+1)/p^l) - 1 of level l (scatter); OFFSET = 0:
+// entry floor(t/p^l) at weight 1/p^l (gather+pool backward).
+template <int L, int OFFSET, typename Tout>
+__device__ __forceinline__ void walk_tokens(const Levels& lv, const int32_t* __restrict__ iv,
+                                            const float* __restrict__ rows, Tout* __restrict__ out,
+                                            int64_t row, int t0, int t1) {
+  float c[L][8];
+  int cj[L];
+  float w[L];
+  w[0] = 1.0f;
+#pragma unroll
+  for (int l = 1; l < L; ++l) {
+    cj[l] = -2;  // no entry cached
+    w[l] = OFFSET ? 1.0f : w[l - 1] / static_cast<float>(lv.p);
+  }
+  for (int tb = t0; tb < t1; tb += 8) {
+    const int tl = (tb + 8 < t1 ? tb + 8 : t1) - 1;  // last token of the batch
+    int32_t s0[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s0[u] = tb + u <= tl ? iv[tb + u] : -1;
+    int32_t pre[L][kPre];
+    int jf[L];
+#pragma unroll
+    for (int l = 1; l < L; ++l) {
+      jf[l] = level_div(lv, l, tb + OFFSET) - OFFSET;
+      const int jl = level_div(lv, l, tl + OFFSET) - OFFSET;
+#pragma unroll
+      for (int i = 0; i < kPre; ++i) {
+        const int j = jf[l] + i;
+        pre[l][i] = (j >= 0 && j <= jl && j != cj[l]) ? iv[lv.off[l] + j] : -1;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = tb + u;
+      if (t > tl) break;
+      float acc[8];
+      if (s0[u] >= 0 && s0[u] < lv.S) {  // level 0: only a few percent of tokens are gathered
+        ld8(rows + static_cast<int64_t>(s0[u]) * lv.D, acc);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+      }
+#pragma unroll
+      for (int l = 1; l < L; ++l) {
+        const int j = level_div(lv, l, t + OFFSET) - OFFSET;
+        if (j != cj[l]) {
+          cj[l] = j;
+          const int32_t sl = pre[l][j - jf[l]];
+          if (sl >= 0 && sl < lv.S) {
+            ld8(rows + static_cast<int64_t>(sl) * lv.D, c[l]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) c[l][e] *= w[l];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) c[l][e] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += c[l][e];
+      }
+      st8(out + static_cast<int64_t>(t) * row, acc);
+    }
+  }
+}
+
+template <int L, typename Tout>
 __global__ __launch_bounds__(256) void scatter_kernel(Levels lv, int64_t Sp,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ og,
                                                       Tout* __restrict__ y) {
-  constexpr int G = D / 8, TPP = 256 / G;  // lanes per row, tokens per pass
-  const int64_t bh = blockIdx.y;
-  const int64_t b = bh / lv.H, h = bh % lv.H;
-  const int g = threadIdx.x % G;
-  const int64_t row = static_cast<int64_t>(lv.H) * D;
-  const int32_t* iv = inv + bh * lv.P;
-  const float* ob = og + bh * Sp * D;
-#pragma unroll
-  for (int pass = 0; pass < kTok / TPP; ++pass) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kTok + pass * TPP + threadIdx.x / G;
-    if (t >= lv.N) continue;
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int l = 0; l < lv.L; ++l) {
-      const int64_t j = (t + 1) / lv.pw[l] - 1;
-      if (j < 0) continue;
-      const int32_t s = iv[lv.off[l] + j];
-      if (s < 0 || s >= lv.S) continue;
-      float v[8];
-      ld8(ob + static_cast<int64_t>(s) * D + g * 8, v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += v[e];
-    }
-    st8(y + (b * lv.N + t) * row + h * D + g * 8, acc);
-  }
+  const int hd8 = lv.D / 8;
+  const int64_t G = static_cast<int64_t>(lv.H) * hd8;  // column groups per token row
+  const int64_t runs = (lv.N + kRun - 1) / kRun;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= lv.B * runs * G) return;
+  const int64_t g = gid % G;
+  const int64_t rr = gid / G;
+  const int64_t b = rr / runs;
+  const int64_t t0 = (rr % runs) * kRun;
+  const int64_t t1 = t0 + kRun < lv.N ? t0 + kRun : lv.N;
+  const int64_t bh = b * lv.H + g / hd8;
+  walk_tokens<L, 1>(lv, inv + bh * lv.P, og + bh * Sp * lv.D + (g % hd8) * 8,
+                    y + b * lv.N * G * 8 + g * 8, G * 8, static_cast<int>(t0),
+                    static_cast<int>(t1));
 }
 
 // -------------------------------------------------------------------- scatter backward
@@ -102,9 +167,10 @@ __global__ __launch_bounds__(256) void scatter_bwd_kernel(
   constexpr int TS = 64;       // slots per workgroup (transposed writes are 128 B)
   constexpr int LR = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t tile[TS * LR];
-  const int64_t bh = blockIdx.y;
+  const int64_t BH = lv.B * lv.H;
+  const int64_t bh = blockIdx.x % BH;  // heads fastest: neighbouring slot ranges of all heads
   const int64_t b = bh / lv.H, h = bh % lv.H;
-  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * TS;
+  const int64_t s0 = static_cast<int64_t>(blockIdx.x / BH) * TS;
   const int g = threadIdx.x % G;
   const int64_t row = static_cast<int64_t>(lv.H) * D;
   const Tin* yb = dy + b * lv.N * row + h * D + g * 8;
@@ -159,54 +225,50 @@ __global__ __launch_bounds__(256) void scatter_bwd_kernel(
 }
 
 // ------------------------------------------------------------- gather + pool backward
-template <int D, typename Tout>
+// Token-walking layout of scatter_kernel; blockIdx.y selects Q, K or V.
+template <int L, typename Tout>
 __global__ __launch_bounds__(256) void gather_pool_bwd_kernel(
     Levels lv, int64_t Sp, const int32_t* __restrict__ inv, const float* __restrict__ g0,
     const float* __restrict__ g1, const float* __restrict__ g2, Tout* __restrict__ d0,
     Tout* __restrict__ d1, Tout* __restrict__ d2) {
-  constexpr int G = D / 8, TPP = 256 / G;
-  const int64_t bh = blockIdx.y;
-  const int64_t b = bh / lv.H, h = bh % lv.H;
-  const int which = blockIdx.z;
+  const int which = blockIdx.y;
   const float* gx = which == 0 ? g0 : (which == 1 ? g1 : g2);
   Tout* dx = which == 0 ? d0 : (which == 1 ? d1 : d2);
-  const int g = threadIdx.x % G;
-  const int64_t row = static_cast<int64_t>(lv.H) * D;
-  const int32_t* iv = inv + bh * lv.P;
-  const float* gb = gx + bh * Sp * D;
-#pragma unroll
-  for (int pass = 0; pass < kTok / TPP; ++pass) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kTok + pass * TPP + threadIdx.x / G;
-    if (t >= lv.N) continue;
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    float w = 1.0f;
-    for (int l = 0; l < lv.L; ++l) {
-      const int32_t s = iv[lv.off[l] + t / lv.pw[l]];
-      if (s >= 0 && s < lv.S) {
-        float v[8];
-        ld8(gb + static_cast<int64_t>(s) * D + g * 8, v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(v[e], w, acc[e]);
-      }
-      w /= static_cast<float>(lv.p);
-    }
-    st8(dx + (b * lv.N + t) * row + h * D + g * 8, acc);
-  }
+  const int hd8 = lv.D / 8;
+  const int64_t G = static_cast<int64_t>(lv.H) * hd8;
+  const int64_t runs = (lv.N + kRun - 1) / kRun;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= lv.B * runs * G) return;
+  const int64_t g = gid % G;
+  const int64_t rr = gid / G;
+  const int64_t b = rr / runs;
+  const int64_t t0 = (rr % runs) * kRun;
+  const int64_t t1 = t0 + kRun < lv.N ? t0 + kRun : lv.N;
+  const int64_t bh = b * lv.H + g / hd8;
+  walk_tokens<L, 0>(lv, inv + bh * lv.P, gx + bh * Sp * lv.D + (g % hd8) * 8,
+                    dx + b * lv.N * G * 8 + g * 8, G * 8, static_cast<int>(t0),
+                    static_cast<int>(t1));
 }
 
 template <typename Tout>
 hipError_t scatter_t(const Levels& lv, const int32_t* inv, const float* og, void* y,
                      hipStream_t st) {
   const int64_t Sp = padded_len(lv.S);
-  dim3 grid(static_cast<unsigned>((lv.N + kTok - 1) / kTok), static_cast<unsigned>(lv.B * lv.H));
-  if (lv.D == 64)
-    hipLaunchKernelGGL((scatter_kernel<64, Tout>), grid, dim3(256), 0, st, lv, Sp, inv, og,
-                       static_cast<Tout*>(y));
-  else
-    hipLaunchKernelGGL((scatter_kernel<128, Tout>), grid, dim3(256), 0, st, lv, Sp, inv, og,
-                       static_cast<Tout*>(y));
+  const int64_t threads = lv.B * ((lv.N + kRun - 1) / kRun) * lv.H * (lv.D / 8);
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, lv, Sp, inv, og, static_cast<Tout*>(y));
+  };
+  switch (lv.L) {
+    case 1: go(scatter_kernel<1, Tout>); break;
+    case 2: go(scatter_kernel<2, Tout>); break;
+    case 3: go(scatter_kernel<3, Tout>); break;
+    case 4: go(scatter_kernel<4, Tout>); break;
+    case 5: go(scatter_kernel<5, Tout>); break;
+    case 6: go(scatter_kernel<6, Tout>); break;
+    case 7: go(scatter_kernel<7, Tout>); break;
+    default: go(scatter_kernel<8, Tout>); break;
+  }
   return hipGetLastError();
 }
 
@@ -214,7 +276,7 @@ template <typename Tin>
 hipError_t scatter_bwd_t(const Levels& lv, const int32_t* gmap, const float* og, const void* dy,
                          void* dog, void* dogt, float* delta, hipStream_t st) {
   const int64_t Sp = padded_len(lv.S);
-  dim3 grid(static_cast<unsigned>(Sp / 64), static_cast<unsigned>(lv.B * lv.H));
+  dim3 grid(static_cast<unsigned>(Sp / 64 * lv.B * lv.H));
   auto* a = static_cast<uint16_t*>(dog);
   auto* at = static_cast<uint16_t*>(dogt);
   if (lv.D == 64)
@@ -230,16 +292,22 @@ template <typename Tout>
 hipError_t gpb_t(const Levels& lv, const int32_t* inv, const float* a, const float* b,
                  const float* c, void* x, void* y, void* z, hipStream_t st) {
   const int64_t Sp = padded_len(lv.S);
-  dim3 grid(static_cast<unsigned>((lv.N + kTok - 1) / kTok), static_cast<unsigned>(lv.B * lv.H),
-            3);
-  if (lv.D == 64)
-    hipLaunchKernelGGL((gather_pool_bwd_kernel<64, Tout>), grid, dim3(256), 0, st, lv, Sp, inv,
-                       a, b, c, static_cast<Tout*>(x), static_cast<Tout*>(y),
-                       static_cast<Tout*>(z));
-  else
-    hipLaunchKernelGGL((gather_pool_bwd_kernel<128, Tout>), grid, dim3(256), 0, st, lv, Sp, inv,
-                       a, b, c, static_cast<Tout*>(x), static_cast<Tout*>(y),
-                       static_cast<Tout*>(z));
+  const int64_t threads = lv.B * ((lv.N + kRun - 1) / kRun) * lv.H * (lv.D / 8);
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256), 3);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, lv, Sp, inv, a, b, c,
+                       static_cast<Tout*>(x), static_cast<Tout*>(y), static_cast<Tout*>(z));
+  };
+  switch (lv.L) {
+    case 1: go(gather_pool_bwd_kernel<1, Tout>); break;
+    case 2: go(gather_pool_bwd_kernel<2, Tout>); break;
+    case 3: go(gather_pool_bwd_kernel<3, Tout>); break;
+    case 4: go(gather_pool_bwd_kernel<4, Tout>); break;
+    case 5: go(gather_pool_bwd_kernel<5, Tout>); break;
+    case 6: go(gather_pool_bwd_kernel<6, Tout>); break;
+    case 7: go(gather_pool_bwd_kernel<7, Tout>); break;
+    default: go(gather_pool_bwd_kernel<8, Tout>); break;
+  }
   return hipGetLastError();
 }
 
