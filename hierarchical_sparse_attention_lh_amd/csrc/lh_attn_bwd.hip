@@ -184,9 +184,9 @@ __device__ __forceinline__ void attn_bwd_q_body(
     const uint16_t* __restrict__ dout, float* __restrict__ dq, int S, int Sp, int64_t BH,
     float scale, float sl2) {
   constexpr int BM = 128, BN = 64;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t kts[2][D * BN];
+  __shared__ __attribute__((aligned(16))) uint16_t ks0[BN * D], ks1[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs0[BN * D], vs1[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t kts0[D * BN], kts1[D * BN];
 
   const int nqt = Sp / BM;
   const int64_t item = xcd_item(blockIdx.x, BH * nqt);
@@ -218,14 +218,19 @@ __device__ __forceinline__ void attn_bwd_q_body(
   const int kend = S < Q0 + BM ? S : Q0 + BM;
   const int nkt = (kend + BN - 1) / BN;
 
-  auto stage = [&](int t, int buf) {
+  auto stage = [&](int t, auto bufc) {
+    constexpr bool B1 = decltype(bufc)::value;
     const int k0 = t * BN;
-    stage_tile<BN, D, 256>(kb + static_cast<int64_t>(k0) * D, D, ks[buf], tid);
-    stage_tile<BN, D, 256>(vb + static_cast<int64_t>(k0) * D, D, vs[buf], tid);
-    stage_tile<D, BN, 256>(ktb + k0, Sp, kts[buf], tid);
+    stage_tile<BN, D, 256>(kb + static_cast<int64_t>(k0) * D, D, B1 ? ks1 : ks0, tid);
+    stage_tile<BN, D, 256>(vb + static_cast<int64_t>(k0) * D, D, B1 ? vs1 : vs0, tid);
+    stage_tile<D, BN, 256>(ktb + k0, Sp, B1 ? kts1 : kts0, tid);
   };
 
-  auto tile = [&](auto masked, int t, int buf) {
+  auto tile = [&](auto masked, int t, auto bufc) {
+    constexpr bool B1 = decltype(bufc)::value;
+    const uint16_t* ksb = B1 ? ks1 : ks0;
+    const uint16_t* vsb = B1 ? vs1 : vs0;
+    const uint16_t* ktsb = B1 ? kts1 : kts0;
     const int k0 = t * BN;
     f32x16 sacc[2], pacc[2];
 #pragma unroll
@@ -234,8 +239,8 @@ __device__ __forceinline__ void attn_bwd_q_body(
       pacc[b2] = zero16();
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        sacc[b2] = mfma32(lds_op<D>(ks[buf], b2 * 32 + lq, 2 * kk + hl), qreg[kk], sacc[b2]);
-        pacc[b2] = mfma32(lds_op<D>(vs[buf], b2 * 32 + lq, 2 * kk + hl), oreg[kk], pacc[b2]);
+        sacc[b2] = mfma32(lds_op<D>(ksb, b2 * 32 + lq, 2 * kk + hl), qreg[kk], sacc[b2]);
+        pacc[b2] = mfma32(lds_op<D>(vsb, b2 * 32 + lq, 2 * kk + hl), oreg[kk], pacc[b2]);
       }
     }
 #pragma unroll
@@ -255,26 +260,29 @@ __device__ __forceinline__ void attn_bwd_q_body(
       c_to_op2(pacc[t4 >> 1], t4 & 1, sh, sl);
 #pragma unroll
       for (int d2 = 0; d2 < D / 32; ++d2) {
-        const bf16x8 a = lds_op<BN>(kts[buf], d2 * 32 + lq, 2 * t4 + hl);
+        const bf16x8 a = lds_op<BN>(ktsb, d2 * 32 + lq, 2 * t4 + hl);
         dqacc[d2] = mfma32(a, sl, dqacc[d2]);
         dqacc[d2] = mfma32(a, sh, dqacc[d2]);
       }
     }
   };
 
-  stage(0, 0);
-  wait_vmem();
-  __syncthreads();
-  for (int t = 0; t < nkt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nkt) stage(t + 1, buf ^ 1);
+  auto step = [&](int t, auto bufc) {
+    if (t + 1 < nkt) stage(t + 1, std::integral_constant<bool, !decltype(bufc)::value>{});
     const int k0 = t * BN;
     if (k0 + BN - 1 > qw || k0 + BN > S)
-      tile(std::true_type{}, t, buf);
+      tile(std::true_type{}, t, bufc);
     else
-      tile(std::false_type{}, t, buf);
+      tile(std::false_type{}, t, bufc);
     wait_vmem();
     __syncthreads();
+  };
+  stage(0, std::false_type{});
+  wait_vmem();
+  __syncthreads();
+  for (int t = 0; t < nkt; t += 2) {
+    step(t, std::false_type{});
+    if (t + 1 < nkt) step(t + 1, std::true_type{});
   }
 
   float* dqr = dq + (bh * Sp + myq) * D;

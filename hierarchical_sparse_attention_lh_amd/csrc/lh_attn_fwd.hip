@@ -17,7 +17,10 @@
 //     operand (swap23 layout), so each A operand is one 16-byte LDS read and P never
 //     touches LDS.
 //   * K and V^T tiles are staged with direct global->LDS loads into XOR-swizzled LDS rows,
-//     double-buffered: the next tile is in flight while the current one is multiplied.
+//     double-buffered: the next tile is in flight while the current one is multiplied.  The
+//     two buffers are separate LDS objects and the loop is unrolled by two so each use names
+//     its buffer statically; the compiler then does not make the current tile's LDS reads
+//     wait for the next tile's loads (it only waits at the barrier).
 //   * Only diagonal and ragged-tail tiles evaluate the causal mask.  The running max moves
 //     only when a row's maximum grows by more than 8 (base 2), so most tiles skip the
 //     rescale of the accumulators; the final division by the row sum is exact either way.
@@ -44,8 +47,10 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
                                               float* __restrict__ o, float* __restrict__ lse,
                                               int S, int Sp, int64_t BH, float sl2) {
   constexpr int BM = 128, BN = 64;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][D * BN];
+  __shared__ __attribute__((aligned(16))) uint16_t ks0[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t ks1[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs0[D * BN];
+  __shared__ __attribute__((aligned(16))) uint16_t vs1[D * BN];
 
   const int nqt = Sp / BM;
   const int64_t item = xcd_item(blockIdx.x, BH * nqt);
@@ -73,19 +78,23 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
   const int kend = S < q0 + BM ? S : q0 + BM;
   const int nkt = (kend + BN - 1) / BN;
 
-  auto stage = [&](int t, int buf) {
-    stage_tile<BN, D, 256>(kb + static_cast<int64_t>(t) * BN * D, D, ks[buf], tid);
-    stage_tile<D, BN, 256>(vb + t * BN, Sp, vs[buf], tid);
+  auto stage = [&](int t, auto bufc) {
+    uint16_t* kd = decltype(bufc)::value ? ks1 : ks0;
+    uint16_t* vd = decltype(bufc)::value ? vs1 : vs0;
+    stage_tile<BN, D, 256>(kb + static_cast<int64_t>(t) * BN * D, D, kd, tid);
+    stage_tile<D, BN, 256>(vb + t * BN, Sp, vd, tid);
   };
 
-  auto tile = [&](auto masked, int t, int buf) {
+  auto tile = [&](auto masked, int t, auto bufc) {
+    const uint16_t* ksb = decltype(bufc)::value ? ks1 : ks0;
+    const uint16_t* vsb = decltype(bufc)::value ? vs1 : vs0;
     f32x16 sacc[2];
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) {
       sacc[b2] = zero16();
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk)
-        sacc[b2] = mfma32(lds_op<D>(ks[buf], b2 * 32 + lq, 2 * kk + hl), qreg[kk], sacc[b2]);
+        sacc[b2] = mfma32(lds_op<D>(ksb, b2 * 32 + lq, 2 * kk + hl), qreg[kk], sacc[b2]);
     }
     if constexpr (decltype(masked)::value) {
       const int k0 = t * BN;
@@ -137,26 +146,29 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
       c_to_op2(sacc[t4 >> 1], t4 & 1, ph, pl);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 a = lds_op<BN>(vs[buf], db * 32 + lq, 2 * t4 + hl);
+        const bf16x8 a = lds_op<BN>(vsb, db * 32 + lq, 2 * t4 + hl);
         oacc[db] = mfma32(a, pl, oacc[db]);
         oacc[db] = mfma32(a, ph, oacc[db]);
       }
     }
   };
 
-  stage(0, 0);
-  wait_vmem();
-  __syncthreads();
-  for (int t = 0; t < nkt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nkt) stage(t + 1, buf ^ 1);
+  auto step = [&](int t, auto bufc) {
+    if (t + 1 < nkt) stage(t + 1, std::integral_constant<bool, !decltype(bufc)::value>{});
     const int k0 = t * BN;
     if (k0 + BN - 1 > qw || k0 + BN > S)
-      tile(std::true_type{}, t, buf);
+      tile(std::true_type{}, t, bufc);
     else
-      tile(std::false_type{}, t, buf);
+      tile(std::false_type{}, t, bufc);
     wait_vmem();
     __syncthreads();
+  };
+  stage(0, std::false_type{});
+  wait_vmem();
+  __syncthreads();
+  for (int t = 0; t < nkt; t += 2) {
+    step(t, std::false_type{});
+    if (t + 1 < nkt) step(t + 1, std::true_type{});
   }
 
   const float l_own = l_run - l_cmp;

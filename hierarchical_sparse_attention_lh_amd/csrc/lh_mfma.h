@@ -43,11 +43,14 @@ __device__ __forceinline__ bf16x8 ld_op8x2(const uint16_t* p0, const uint16_t* p
   return as_bf16x8(u);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded (to nearest even) to bf16 and packed, a in the low half.  Written as one
+// vector conversion so it becomes a single two-source v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
-  const __bf16 x = static_cast<__bf16>(a);
-  const __bf16 y = static_cast<__bf16>(b);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, y)) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // C registers 8*half .. 8*half+7 of one 32x32 tile, rounded to bf16, as a B (or A) operand.
