@@ -78,17 +78,17 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
   const int kend = S < q0 + BM ? S : q0 + BM;
   const int nkt = (kend + BN - 1) / BN;
 
-  auto stage = [&](int t, auto bufc) {
-    uint16_t* kd = decltype(bufc)::value ? ks1 : ks0;
-    uint16_t* vd = decltype(bufc)::value ? vs1 : vs0;
-    stage_tile<BN, D, 256>(kb + static_cast<int64_t>(t) * BN * D, D, kd, tid);
-    stage_tile<D, BN, 256>(vb + t * BN, Sp, vd, tid);
+  auto stage_k = [&](int t, auto bufc) {
+    stage_tile<BN, D, 256>(kb + static_cast<int64_t>(t) * BN * D, D,
+                           decltype(bufc)::value ? ks1 : ks0, tid);
+  };
+  auto stage_v = [&](int t, auto bufc) {
+    stage_tile<D, BN, 256>(vb + t * BN, Sp, decltype(bufc)::value ? vs1 : vs0, tid);
   };
 
-  auto tile = [&](auto masked, int t, auto bufc) {
+  // S^T of one key tile: 32 keys x 32 queries per C block, two blocks.
+  auto scores = [&](f32x16 (&sacc)[2], auto bufc) {
     const uint16_t* ksb = decltype(bufc)::value ? ks1 : ks0;
-    const uint16_t* vsb = decltype(bufc)::value ? vs1 : vs0;
-    f32x16 sacc[2];
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) {
       sacc[b2] = zero16();
@@ -96,6 +96,28 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
       for (int kk = 0; kk < D / 16; ++kk)
         sacc[b2] = mfma32(lds_op<D>(ksb, b2 * 32 + lq, 2 * kk + hl), qreg[kk], sacc[b2]);
     }
+  };
+
+  // Online softmax of score tile t and its P V^T product, with the score product of tile t+1
+  // (into nxt, from K buffer !odd) woven into the same instruction stream.  While an MFMA
+  // occupies a SIMD's matrix core, the vector instructions that overlap it come from the
+  // issuing wave, so the code is laid out as short chunks of one MFMA plus the vector work
+  // that can run behind it, and sched_barrier keeps the compiler from regrouping them.
+  auto soft_pv = [&](auto masked, int t, f32x16 (&sacc)[2], f32x16 (&nxt)[2], auto par) {
+    constexpr bool odd = decltype(par)::value;
+    const uint16_t* vsb = odd ? vs1 : vs0;
+    const uint16_t* ksn = odd ? ks0 : ks1;
+    // operands of both products; the LDS latency hides behind the row max
+    bf16x8 ka[2][D / 16], va[4][D / 32];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) ka[b2][kk] = lds_op<D>(ksn, b2 * 32 + lq, 2 * kk + hl);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        va[t4][db] = lds_op<BN>(vsb, db * 32 + lq, 2 * t4 + hl);
     if constexpr (decltype(masked)::value) {
       const int k0 = t * BN;
 #pragma unroll
@@ -111,7 +133,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[b2][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    mx = pair_max(mx) * sl2;
     const bool grow = mx > m_run + kSlack;
     if (__any(grow)) {
       const float m_new = grow ? mx : m_run;
@@ -124,55 +146,95 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
       l_cmp *= alpha;
       m_run = m_new;
     }
+    // score MFMAs of tile t+1, each with a quarter of the exponentials of tile t behind it
+    constexpr int NS = 2 * (D / 16);  // score MFMAs per tile
+    constexpr int EPC = 32 / NS;       // exponentials per chunk
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
+    for (int b2 = 0; b2 < 2; ++b2) nxt[b2] = zero16();
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        sacc[b2][r] = __builtin_amdgcn_exp2f(fmaf(sacc[b2][r], sl2, -m_run));
+    for (int i = 0; i < NS; ++i) {
+      const int kk = i >> 1, b2 = i & 1;
+      nxt[b2] = mfma32(ka[b2][kk], qreg[kk], nxt[b2]);
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) {
+        const int e = i * EPC + u, eb = e >> 4, er = e & 15;
+        sacc[eb][er] = __builtin_amdgcn_exp2f(fmaf(sacc[eb][er], sl2, -m_run));
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2 * EPC, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // P V^T: the split of chunk t4 + 1 and the row sum run behind the MFMAs of chunk t4
+    bf16x8 ph[4], pl[4];
+    c_to_op2(sacc[0], 0, ph[0], pl[0]);
     float part[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) part[r] = sacc[0][r] + sacc[1][r];
-#pragma unroll
-    for (int w2 = 8; w2 >= 1; w2 >>= 1)
-#pragma unroll
-      for (int r = 0; r < w2; ++r) part[r] += part[r + w2];
-    const float yk = part[0] - l_cmp;
-    const float tk = l_run + yk;
-    l_cmp = (tk - l_run) - yk;
-    l_run = tk;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
-      bf16x8 ph, pl;
-      c_to_op2(sacc[t4 >> 1], t4 & 1, ph, pl);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 a = lds_op<BN>(vsb, db * 32 + lq, 2 * t4 + hl);
-        oacc[db] = mfma32(a, pl, oacc[db]);
-        oacc[db] = mfma32(a, ph, oacc[db]);
+      for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32(va[t4][db], pl[t4], oacc[db]);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32(va[t4][db], ph[t4], oacc[db]);
+      if (t4 < 3) c_to_op2(sacc[(t4 + 1) >> 1], (t4 + 1) & 1, ph[t4 + 1], pl[t4 + 1]);
+      if (t4 == 0) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) part[r] += part[r + 8];
+      } else if (t4 == 1) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[r] += part[r + 4];
+      } else if (t4 == 2) {
+        part[0] += part[2];
+        part[1] += part[3];
+        part[0] += part[1];
+      } else {
+        const float yk = part[0] - l_cmp;
+        const float tk = l_run + yk;
+        l_cmp = (tk - l_run) - yk;
+        l_run = tk;
       }
+#pragma unroll
+      for (int i = 0; i < 2 * (D / 32); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  auto step = [&](int t, auto bufc) {
-    if (t + 1 < nkt) stage(t + 1, std::integral_constant<bool, !decltype(bufc)::value>{});
+  // Software pipeline: while the softmax of tile t runs on the vector ALUs, the score
+  // product of tile t+1 runs on the matrix cores.  LDS holds K(t+1) and V(t) during step t;
+  // K(t+2) and V(t+1) are loaded into the buffers freed by step t-1.  At the last step the
+  // score product reads a stale K buffer and its result is never used.
+  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto par) {
+    constexpr bool odd = decltype(par)::value;
+    if (t + 2 < nkt) stage_k(t + 2, std::integral_constant<bool, odd>{});
+    if (t + 1 < nkt) stage_v(t + 1, std::integral_constant<bool, !odd>{});
     const int k0 = t * BN;
     if (k0 + BN - 1 > qw || k0 + BN > S)
-      tile(std::true_type{}, t, bufc);
+      soft_pv(std::true_type{}, t, cur, nxt, par);
     else
-      tile(std::false_type{}, t, bufc);
+      soft_pv(std::false_type{}, t, cur, nxt, par);
     wait_vmem();
     __syncthreads();
   };
-  stage(0, std::false_type{});
+
+  f32x16 sa[2], sb[2];
+  stage_k(0, std::false_type{});
+  stage_v(0, std::false_type{});
+  if (nkt > 1) stage_k(1, std::true_type{});
   wait_vmem();
   __syncthreads();
+  scores(sa, std::false_type{});
+  __syncthreads();  // K(0)'s buffer is refilled by the first step
   for (int t = 0; t < nkt; t += 2) {
-    step(t, std::false_type{});
-    if (t + 1 < nkt) step(t + 1, std::true_type{});
+    step(t, sa, sb, std::false_type{});
+    if (t + 1 < nkt) step(t + 1, sb, sa, std::true_type{});
   }
 
   const float l_own = l_run - l_cmp;
-  const float l_tot = l_own + __shfl_xor(l_own, 32);
+  const float l_tot = pair_sum(l_own);
   const float inv_l = 1.0f / l_tot;
   float* orow = o + (bh * Sp + myq) * D;
 #pragma unroll
@@ -188,7 +250,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
 
 // D = 64 fits three waves per SIMD (134 VGPRs), so MFMA work of one wave overlaps the
 // softmax arithmetic of the others; D = 128 keeps the compiler's default.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attn_fwd_d64(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
              const uint16_t* __restrict__ vt, float* __restrict__ o, float* __restrict__ lse,
              int S, int Sp, int64_t BH, float sl2) {

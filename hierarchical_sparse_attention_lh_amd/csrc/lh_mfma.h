@@ -104,14 +104,23 @@ __host__ __device__ __forceinline__ int64_t swap23(int64_t s) {
   return (s & ~int64_t(12)) | ((s & 4) << 1) | ((s & 8) >> 1);
 }
 
-// LDS tiles are unpadded rows whose 16-byte chunks are XOR-swizzled with (row & 7): eight
-// consecutive rows read at one logical chunk index touch eight different bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+// LDS tiles are unpadded rows whose 16-byte chunks are XOR-swizzled.  The LDS serves a
+// 16-byte-per-lane read 16 lanes at a time from 64 four-byte banks, i.e. sixteen 16-byte bank
+// groups; the operand reads have 16 consecutive lanes on 16 consecutive rows at one logical
+// chunk, so the swizzle makes those 16 (row, chunk) pairs land in 16 different groups.  A
+// 128-byte row (64 bf16) fills half a bank line, so rows 2j and 2j+1 share the XOR key j;
+// a 256-byte row (128 bf16) fills a whole line and each of 16 rows gets its own key.
+template <int ROW_ELEMS>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  constexpr int CPR = ROW_ELEMS / 8;                // 16-byte chunks per row
+  constexpr int RPL = CPR >= 16 ? 1 : 16 / CPR;     // rows per 256-byte bank line
+  return chunk ^ ((row / RPL) % CPR);
+}
 
 // 16-byte MFMA operand: logical chunk `chunk` of `row` in a swizzled LDS tile.
 template <int ROW_ELEMS>
 __device__ __forceinline__ bf16x8 lds_op(const uint16_t* tile, int row, int chunk) {
-  return ld_op16(tile + row * ROW_ELEMS + (swz(row, chunk) << 3));
+  return ld_op16(tile + row * ROW_ELEMS + (swz<ROW_ELEMS>(row, chunk) << 3));
 }
 
 // Stage ROWS x ROW_ELEMS bf16 (row stride `gstride` elements in global memory) into a swizzled
@@ -130,7 +139,7 @@ __device__ __forceinline__ void stage_tile(const uint16_t* g, int64_t gstride, u
     const int base = (i * (NT / 64) + wave) * 64;  // first LDS chunk of this wave instruction
     const int lin = base + lane;
     const int row = lin / CPR, pc = lin % CPR;
-    const int c = pc ^ (row & 7);
+    const int c = swz<ROW_ELEMS>(row, pc);
     __builtin_amdgcn_global_load_lds(g + row * gstride + c * 8, lds + base * 8, 16, 0, 0);
   }
 }
@@ -138,6 +147,19 @@ __device__ __forceinline__ void stage_tile(const uint16_t* g, int64_t gstride, u
 // 64 floats into LDS with one wave instruction (4 bytes per lane).
 __device__ __forceinline__ void stage_f32x64(const float* g, float* lds, int lane) {
   __builtin_amdgcn_global_load_lds(g + lane, lds, 4, 0, 0);
+}
+
+// Lanes l and l ^ 32 exchange a value with one v_permlane32_swap (no LDS round trip); the
+// swap leaves {x[l], x[l ^ 32]} in every lane, so symmetric reductions need no select.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
