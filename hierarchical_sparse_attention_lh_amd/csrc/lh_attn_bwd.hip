@@ -70,7 +70,10 @@ __device__ __forceinline__ void attn_bwd_kv_body(
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     kreg[kk] = ld_op16(k + (bh * Sp + mykey) * D + 16 * kk + hl * 8);
-    vreg[kk] = ld_op16(v + (bh * Sp + mykey) * D + 16 * kk + hl * 8);
+    // -V: the dP product then accumulates Delta - dP on top of Delta (see tile)
+    vreg[kk] = as_bf16x8(__builtin_bit_cast(u32x4, ld_op16(v + (bh * Sp + mykey) * D +
+                                                           16 * kk + hl * 8)) ^
+                         0x80008000u);
   }
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
@@ -94,26 +97,34 @@ __device__ __forceinline__ void attn_bwd_kv_body(
 
   auto tile = [&](auto masked, int t, int buf) {
     const int q0 = t * BQ;
+    // The C rows of a lane are queries b2*32 + g*8 + (l/32)*4 + [0..3] (g = r/4): four float4
+    // reads give a lane its 16 per-row values of lse or Delta in register order.
     f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) {
       sacc[b2] = zero16();
-      pacc[b2] = zero16();
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 d4 = *reinterpret_cast<const float4*>(&dl[buf][b2 * 32 + g * 8 + hl * 4]);
+        pacc[b2][4 * g] = d4.x;
+        pacc[b2][4 * g + 1] = d4.y;
+        pacc[b2][4 * g + 2] = d4.z;
+        pacc[b2][4 * g + 3] = d4.w;
+      }
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         sacc[b2] = mfma32(lds_op<D>(qs[buf], b2 * 32 + lq, 2 * kk + hl), kreg[kk], sacc[b2]);
         pacc[b2] = mfma32(lds_op<D>(ds_[buf], b2 * 32 + lq, 2 * kk + hl), vreg[kk], pacc[b2]);
       }
     }
+    // pacc now holds Delta - dP, so p * pacc = -dS (the sign is folded into the final scale)
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int qi = b2 * 32 + g * 8 + hl * 4;  // 4 consecutive local queries
         const float4 l4 = *reinterpret_cast<const float4*>(&ls[buf][qi]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&dl[buf][qi]);
-        const float lv4[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float lv4[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = g * 4 + u;
@@ -123,7 +134,7 @@ __device__ __forceinline__ void attn_bwd_kv_body(
             if (qa < mykey || qa >= S) p = 0.f;
           }
           sacc[b2][r] = p;
-          pacc[b2][r] = p * (pacc[b2][r] - dv4[u]);
+          pacc[b2][r] = p * pacc[b2][r];
         }
       }
 #pragma unroll
@@ -165,8 +176,9 @@ __device__ __forceinline__ void attn_bwd_kv_body(
   for (int d2 = 0; d2 < D / 32; ++d2)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      float4 a = make_float4(dkacc[d2][4 * g] * scale, dkacc[d2][4 * g + 1] * scale,
-                             dkacc[d2][4 * g + 2] * scale, dkacc[d2][4 * g + 3] * scale);
+      const float ns = -scale;  // dkacc holds -dS^T Q
+      float4 a = make_float4(dkacc[d2][4 * g] * ns, dkacc[d2][4 * g + 1] * ns,
+                             dkacc[d2][4 * g + 2] * ns, dkacc[d2][4 * g + 3] * ns);
       float4 b = make_float4(dvacc[d2][4 * g], dvacc[d2][4 * g + 1], dvacc[d2][4 * g + 2],
                              dvacc[d2][4 * g + 3]);
       if (!live) a = b = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -208,7 +220,7 @@ __device__ __forceinline__ void attn_bwd_q_body(
     qreg[kk] = ld_op16(q + (bh * Sp + myq) * D + 16 * kk + hl * 8);
     oreg[kk] = ld_op16(dout + (bh * Sp + myq) * D + 16 * kk + hl * 8);
   }
-  const float l2 = lse[bh * Sp + myq] * kLog2e;
+  const float l2 = lse[bh * Sp + myq];  // base-2 log-sum-exp
   const float dlt = delta[bh * Sp + myq];
 
   f32x16 dqacc[D / 32];

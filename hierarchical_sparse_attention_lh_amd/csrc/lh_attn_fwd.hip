@@ -37,7 +37,6 @@ namespace lh {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;  // base-2 growth of the row max tolerated before a rescale
 
 template <int D>
@@ -245,7 +244,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
                                      oacc[db][4 * g + 2] * inv_l, oacc[db][4 * g + 3] * inv_l);
       *reinterpret_cast<float4*>(orow + db * 32 + g * 8 + hl * 4) = val;
     }
-  if (hl == 0) lse[bh * Sp + myq] = m_run * kLn2 + __logf(l_tot);
+  if (hl == 0) lse[bh * Sp + myq] = m_run + log2f(l_tot);  // base-2 log-sum-exp
 }
 
 // D = 64 fits three waves per SIMD (134 VGPRs), so MFMA work of one wave overlaps the

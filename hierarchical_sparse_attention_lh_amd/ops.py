@@ -146,7 +146,8 @@ def attn_desc(batch, heads, seq, head_dim, scale=0.0) -> LhAttnDesc:
 
 
 def lh_attn_fwd(desc: LhAttnDesc, q, k, vt):
-    """q, k [B, H, Sp, D] bf16, vt [B, H, D, Sp] bf16 -> (o [B, H, Sp, D] f32, lse [B, H, Sp])."""
+    """q, k [B, H, Sp, D] bf16, vt [B, H, D, Sp] bf16 -> (o [B, H, Sp, D] f32, lse [B, H, Sp]);
+    lse is the base-2 log-sum-exp of each row (natural log-sum-exp times log2(e))."""
     b, h, sp, d = q.shape
     o = torch.empty((b, h, sp, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((b, h, sp), dtype=torch.float32, device=q.device)

@@ -200,8 +200,9 @@ typedef struct lh_attn_desc {
   float scale;                         /* <= 0 selects 1/sqrt(D)                        */
 } lh_attn_desc;
 
-/* Og[s] = sum_{s' <= s} softmax(scale * q[s].k[s']) v[s'];  lse[s] = natural-log
- * log-sum-exp of the scaled logits of row s.
+/* Og[s] = sum_{s' <= s} softmax(scale * q[s].k[s']) v[s'];  lse[s] = log2 of
+ * sum_{s' <= s} 2^(scale * log2(e) * q[s].k[s']), the row's log-sum-exp in base 2 (the natural
+ * log-sum-exp times log2(e)): the statistic the backward passes consume directly.
  *   q, k device bf16 [B, H, Sp, D];  vt device bf16 [B, H, D, Sp]  (finite padding)
  *   o    device float32 [B, H, Sp, D];  lse device float32 [B, H, Sp]; padding rows get
  *        the (finite) result of attending over all S keys */

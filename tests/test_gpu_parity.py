@@ -234,6 +234,7 @@ def test_attention_forward(seq, d):
         ro, rl = O.causal_attention(qq, kk, vv, d ** -0.5)
         bound, _ = O.causal_attention(qq, kk, np.abs(vv), d ** -0.5)
         go, gl = f64(o[0, h, :seq]), f64(lse[0, h, :seq])
+        rl = rl / np.log(2.0)  # the kernel reports the log-sum-exp in base 2
         # P enters as a bf16 hi/lo pair (relative error <= 2^-16): the rest is float32 rounding
         err = np.abs(go - ro)
         print(f"attn fwd S={seq} D={d} h={h}: max |dO| {err.max():.2e}, worst err/bound "
