@@ -97,11 +97,40 @@ __device__ __forceinline__ void level1(const Ctx<Tin, Tout>& c, int64_t t0, floa
   for (int e = 0; e < 8; ++e) out[e] = acc[e] * c.inv_p;
 }
 
+// Level-2 block for p = 4: all 16 token loads are issued before any arithmetic or store, so
+// the stores of one block's pooled rows do not hold back the next block's loads.
+template <typename Tin, typename Tout>
+__device__ __forceinline__ void level2_p4(const Ctx<Tin, Tout>& c, const Levels& lv, int64_t t0,
+                                          float (&out)[8]) {
+  float v[16][8];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) load8(c.x + (t0 + u) * c.row, v[u]);
+  float acc2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc2[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float m[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      m[e] = (((v[4 * i][e] + v[4 * i + 1][e]) + v[4 * i + 2][e]) + v[4 * i + 3][e]) * c.inv_p;
+    emit(c, lv, 1, (t0 + 4 * i) / lv.pw[1], m);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc2[e] += m[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = acc2[e] * c.inv_p;
+}
+
 template <int LVL, typename Tin, typename Tout>
 __device__ __forceinline__ void pool_block(const Ctx<Tin, Tout>& c, const Levels& lv, int64_t t0,
                                            float (&out)[8]) {
   if constexpr (LVL == 1) {
     level1(c, t0, out);
+  } else if (LVL == 2 && c.p == 4) {
+    level2_p4(c, lv, t0, out);
+    emit(c, lv, LVL, t0 / lv.pw[LVL], out);
+    return;
   } else {
     float acc[8];
 #pragma unroll
