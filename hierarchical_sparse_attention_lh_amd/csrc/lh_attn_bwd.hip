@@ -33,7 +33,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------- key pass
-template <int D>
+template <int D, int BQ>
 __device__ __forceinline__ void attn_bwd_kv_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ qt,
@@ -41,7 +41,7 @@ __device__ __forceinline__ void attn_bwd_kv_body(
     const uint16_t* __restrict__ dout, const uint16_t* __restrict__ doutt,
     float* __restrict__ dk, float* __restrict__ dv, int S, int Sp, int64_t BH, float scale,
     float sl2) {
-  constexpr int BK = 128, BQ = 64;
+  constexpr int BK = 128, NB = BQ / 32;  // NB blocks of 32 queries per tile
   __shared__ __attribute__((aligned(16))) uint16_t qs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) uint16_t ds_[2][BQ * D];
   __shared__ __attribute__((aligned(16))) uint16_t qts[2][D * BQ];
@@ -91,17 +91,17 @@ __device__ __forceinline__ void attn_bwd_kv_body(
     stage_tile<BQ, D, 256>(db_ + static_cast<int64_t>(q0) * D, D, ds_[buf], tid);
     stage_tile<D, BQ, 256>(qtb + q0, Sp, qts[buf], tid);
     stage_tile<D, BQ, 256>(dtb + q0, Sp, dts[buf], tid);
-    if (wave == 0) stage_f32x64(lb + q0, ls[buf], lane);
-    if (wave == 1) stage_f32x64(dlb + q0, dl[buf], lane);
+    if (wave == 0 && lane < BQ) stage_f32x64(lb + q0, ls[buf], lane);
+    if (wave == 1 && lane < BQ) stage_f32x64(dlb + q0, dl[buf], lane);
   };
 
   auto tile = [&](auto masked, int t, int buf) {
     const int q0 = t * BQ;
     // The C rows of a lane are queries b2*32 + g*8 + (l/32)*4 + [0..3] (g = r/4): four float4
     // reads give a lane its 16 per-row values of lse or Delta in register order.
-    f32x16 sacc[2], pacc[2];
+    f32x16 sacc[NB], pacc[NB];
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) {
+    for (int b2 = 0; b2 < NB; ++b2) {
       sacc[b2] = zero16();
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -119,7 +119,7 @@ __device__ __forceinline__ void attn_bwd_kv_body(
     }
     // pacc now holds Delta - dP, so p * pacc = -dS (the sign is folded into the final scale)
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
+    for (int b2 = 0; b2 < NB; ++b2)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int qi = b2 * 32 + g * 8 + hl * 4;  // 4 consecutive local queries
@@ -138,7 +138,7 @@ __device__ __forceinline__ void attn_bwd_kv_body(
         }
       }
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
+    for (int t4 = 0; t4 < 2 * NB; ++t4) {
       bf16x8 ph, pl, sh, sl;
       c_to_op2(sacc[t4 >> 1], t4 & 1, ph, pl);
       c_to_op2(pacc[t4 >> 1], t4 & 1, sh, sl);
@@ -329,10 +329,12 @@ __device__ __forceinline__ void attn_bwd_q_body(
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attn_bwd_kv_d64(LH_KV_ARGS) {
-  attn_bwd_kv_body<64>(q, k, v, qt, lse, delta, dout, doutt, dk, dv, S, Sp, BH, scale, sl2);
+  attn_bwd_kv_body<64, 64>(q, k, v, qt, lse, delta, dout, doutt, dk, dv, S, Sp, BH, scale,
+                           sl2);
 }
 __global__ __launch_bounds__(256) void attn_bwd_kv_d128(LH_KV_ARGS) {
-  attn_bwd_kv_body<128>(q, k, v, qt, lse, delta, dout, doutt, dk, dv, S, Sp, BH, scale, sl2);
+  attn_bwd_kv_body<128, 32>(q, k, v, qt, lse, delta, dout, doutt, dk, dv, S, Sp, BH, scale,
+                            sl2);
 }
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attn_bwd_q_d64(LH_Q_ARGS) {
