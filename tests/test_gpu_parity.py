@@ -61,8 +61,12 @@ RAGGED = synth.Workload("ragged", 1, 4096, 2, 64, "bf16", 3, 4, 37, 64, 11, True
 WIDE = synth.Workload("wide-d128", 2, 3072, 2, 128, "bf16", 4, 4, 50, 256, 12, True)
 # dense causal attention: one level, S = N
 DENSE = synth.Workload("dense", 1, 640, 2, 64, "bf16", 1, 4, 0, 64, 13, True)
-STAGE_CASES = [TINY, RAGGED, WIDE]
-E2E_CASES = [TINY, RAGGED, WIDE, DENSE]
+# pool factor 2 with five levels (the wider prefetch bound of the token-walking kernels)
+POOL2 = synth.Workload("pool2-l5", 1, 4096, 2, 64, "bf16", 5, 2, 100, 256, 14, True)
+# a pool factor that is not a power of two (division instead of shifts), three chunks
+POOL3 = synth.Workload("pool3", 1, 4608, 2, 64, "bf16", 3, 3, 100, 512, 15, True)
+STAGE_CASES = [TINY, RAGGED, WIDE, POOL2, POOL3]
+E2E_CASES = [TINY, RAGGED, WIDE, DENSE, POOL2, POOL3]
 
 
 def pooled_rows_oracle(x, w):
