@@ -14,6 +14,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -45,9 +46,14 @@ def algorithmic(w, info):
     e = 2 if w.dtype == "bf16" else 4  # token-tensor element size
     BH = B * H
     pairs = BH * S * (S + 1) / 2
+    # scored entries: the pooled levels, plus the raw tokens under the DIRECT reading; the
+    # top-K reads the scores of the selected levels (REFINE: 1..L-1, DIRECT: 0..L-2)
+    n_top = info.level_size[w.levels - 1]
+    scored = P if w.mode == "direct" else P - N
+    selected = P - n_top if w.mode == "direct" else P - N
     by = {
-        "pool_score": 3 * B * N * H * D * e + 3 * B * P1 * H * D * 2 + BH * (P - N) * 4,
-        "topk": BH * (P - N) * 4 + BH * K * 4,
+        "pool_score": 3 * B * N * H * D * e + 3 * B * P1 * H * D * 2 + BH * scored * 4,
+        "topk": BH * selected * 4 + BH * K * 4,
         "build_map": BH * K * 4 + BH * P * 4 + BH * S * 8,
         "gather": BH * S * 4 + 3 * BH * S * D * 2 + 6 * BH * S * D * 2,
         "scatter": BH * S * D * 4 + B * N * H * D * e + BH * N * w.levels * 4,
@@ -146,7 +152,8 @@ def cpu_baseline(w, x):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = 1
-    ocfg = O.Config(w.levels, w.pool, w.k, w.chunk)
+    ocfg = O.Config(w.levels, w.pool, w.k, w.chunk,
+                    mode=O.DIRECT if w.mode == "direct" else O.REFINE)
     q, k, v, dy = (x[n][0, :, 0].astype(np.float64) for n in ("q", "k", "v", "dy"))
     t0 = time.perf_counter()
     _, st = O.head_forward(q, k, v, ocfg)
@@ -165,6 +172,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lh-512k")
+    ap.add_argument("--select", choices=("refine", "direct"), default="refine",
+                    help="selection reading (the metric is quoted on refine)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention baseline")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
@@ -190,6 +199,8 @@ def main():
         del src, dst
 
     w = synth.WORKLOADS[args.workload]
+    if args.select != w.mode:
+        w = dataclasses.replace(w, name=f"{w.name}-{args.select}", mode=args.select)
     log(f"workload {w}")
     t0 = time.perf_counter()
     x = synth.workload_inputs(w, with_grad=True)
@@ -267,7 +278,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_tokens": w.n_tokens, "heads": w.heads,
                    "head_dim": w.head_dim, "levels": w.levels, "pool": w.pool, "k": w.k,
                    "chunk": w.chunk, "gathered_len": info.gathered_len,
-                   "input_dtype": w.dtype, "seed": w.seed},
+                   "input_dtype": w.dtype, "seed": w.seed, "select": w.mode},
         "roofline": roof,
         "cpu_baseline": cpu,
         "forward_tokens_per_s": round(tokens / (fwd_ms * 1e-3), 1),

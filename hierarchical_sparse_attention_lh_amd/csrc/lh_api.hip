@@ -50,8 +50,8 @@ lh_status check_config(const lh_config* c, Levels* lv) {
     return LH_ERR_DTYPE;
   if (c->levels < 1 || c->levels > LH_MAX_LEVELS) return LH_ERR_LEVELS;
   if (c->pool < 2 || c->pool > 16) return LH_ERR_POOL;
-  if (c->select_mode == LH_SEL_DIRECT) return LH_ERR_UNSUPPORTED;
-  if (c->select_mode != LH_SEL_REFINE) return LH_ERR_UNSUPPORTED;
+  if (c->select_mode != LH_SEL_REFINE && c->select_mode != LH_SEL_DIRECT)
+    return LH_ERR_UNSUPPORTED;
   if (c->chunk < 16 || c->chunk > 2048 || (c->chunk & (c->chunk - 1)) != 0) return LH_ERR_CHUNK;
 
   Levels L;
@@ -85,8 +85,13 @@ lh_status check_config(const lh_config* c, Levels* lv) {
   }
   L.P = off;
   L.P1 = poff;
+  // REFINE selects at levels 1..L-1 and a kept entry enters as its p children; DIRECT selects
+  // at levels 0..L-2 and a kept entry enters itself.  The coarsest level always enters whole.
+  L.direct = c->select_mode == LH_SEL_DIRECT;
+  L.sel_first = L.direct ? 0 : 1;
+  L.sel_last = L.direct ? L.L - 2 : L.L - 1;
   int64_t soff = 0, S = L.n[L.L - 1];
-  for (int l = 1; l < L.L; ++l) {  // REFINE: levels 1..L-1 are selected
+  for (int l = L.sel_first; l <= L.sel_last; ++l) {
     if (c->k[l] < 0) return LH_ERR_K;
     const int64_t n = L.n[l];
     if (n > c->chunk && n % c->chunk != 0) return LH_ERR_CHUNK;
@@ -95,7 +100,7 @@ lh_status check_config(const lh_config* c, Levels* lv) {
     L.width[l] = n > c->chunk ? c->chunk : n;
     L.soff[l] = soff;
     soff += L.keff[l];
-    S += L.p * L.keff[l];
+    S += (L.direct ? 1 : L.p) * L.keff[l];
   }
   L.K = soff;
   L.S = S;

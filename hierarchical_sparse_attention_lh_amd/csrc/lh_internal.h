@@ -28,6 +28,10 @@ struct Levels {
   int64_t K;                    // sel_total
   int64_t S;                    // gathered length
   int32_t lg[LH_MAX_LEVELS];    // log2(p^l) when p is a power of two, else -1
+  int32_t direct;               // selection reading: 0 = REFINE (levels 1..L-1, kept entries
+                                // enter as their p children), 1 = DIRECT (levels 0..L-2, kept
+                                // entries enter themselves)
+  int32_t sel_first, sel_last;  // selected levels (sel_first > sel_last when none)
 };
 
 // floor(x / p^l) for non-negative x < 2^31, by a shift when p is a power of two.

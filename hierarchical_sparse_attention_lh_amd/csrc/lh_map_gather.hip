@@ -55,6 +55,9 @@ __device__ __forceinline__ int64_t count_upto(const Levels& lv, const int32_t* s
                                               int64_t T) {
   const int64_t u = (T + 1) / lv.pw[m];  // level-m entries complete by token T
   if (m == lv.L - 1) return u < lv.n[m] ? u : lv.n[m];
+  if (lv.direct) {  // level m entries are the kept entries of level m: count those below u
+    return m <= lv.sel_last ? lower_bound(sel + lv.soff[m], lv.keff[m], u) : 0;
+  }
   // level m entries are the children of kept entries of level m + 1
   const int32_t* kept = sel + lv.soff[m + 1];
   const int64_t nk = lv.keff[m + 1];
@@ -84,7 +87,17 @@ __global__ __launch_bounds__(256) void map_kernel(Levels lv, const int32_t* __re
     m = top;
     i = r;
     own = r;
-  } else {
+  } else if (lv.direct) {  // the kept entries of levels 0..L-2, level by level
+    int64_t rr = r - lv.n[top];
+    int l = 0;
+    while (l < lv.sel_last && rr >= lv.keff[l]) {
+      rr -= lv.keff[l];
+      ++l;
+    }
+    m = l;
+    i = s[lv.soff[l] + rr];
+    own = rr;
+  } else {  // the p children of the kept entries of levels 1..L-1
     int64_t rr = r - lv.n[top];
     int l = 1;
     while (l < top && rr >= lv.p * lv.keff[l]) {

@@ -12,7 +12,8 @@
 // its 8 pooled columns; for the key stream the 8 squares are summed in float64 and reduced
 // over the D/8 lanes of the head with cross-lane shuffles, and one lane writes the score.
 // A wave reads 64 x 16 B = 1 KB of one token row per step: fully coalesced.  Q, K and V are
-// separate grid rows (blockIdx.y) so the three streams run concurrently.
+// separate grid rows (blockIdx.y) so the three streams run concurrently.  Under the DIRECT
+// selection reading the raw key rows (level 0) are scored as well.
 #include "lh_internal.h"
 
 namespace lh {
@@ -59,25 +60,33 @@ struct Ctx {
   float inv_p;
   int hd8;         // D / 8 lanes per head
   bool writer;     // first lane of the head
+  bool score0;     // also score the raw tokens (level 0; DIRECT selection reads them)
 };
+
+// l2 norm of entry (level, j) of this head: the thread's 8 squares in float64, reduced over
+// the head's D/8 lanes, written by the head's first lane.
+template <typename Tin, typename Tout>
+__device__ __forceinline__ void score(const Ctx<Tin, Tout>& c, const Levels& lv, int level,
+                                      int64_t j, const float (&v)[8]) {
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss += static_cast<double>(v[i]) * static_cast<double>(v[i]);
+  for (int m = 1; m < c.hd8; m <<= 1) ss += __shfl_xor(ss, m);
+  if (c.writer) c.sc[lv.off[level] + j] = static_cast<float>(sqrt(ss));
+}
 
 template <typename Tin, typename Tout>
 __device__ __forceinline__ void emit(const Ctx<Tin, Tout>& c, const Levels& lv, int level,
                                      int64_t j, const float (&v)[8]) {
   if (c.px) store8(c.px + (lv.poff[level] + j) * c.row, v);
-  if (c.sc) {
-    double ss = 0.0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss += static_cast<double>(v[i]) * static_cast<double>(v[i]);
-    for (int m = 1; m < c.hd8; m <<= 1) ss += __shfl_xor(ss, m);
-    if (c.writer) c.sc[lv.off[level] + j] = static_cast<float>(sqrt(ss));
-  }
+  if (c.sc) score(c, lv, level, j, v);
 }
 
 // Mean over the p tokens starting at token t0 (level 1); loads are issued four at a time so
 // that several 16-byte requests per thread are in flight.
 template <typename Tin, typename Tout>
-__device__ __forceinline__ void level1(const Ctx<Tin, Tout>& c, int64_t t0, float (&out)[8]) {
+__device__ __forceinline__ void level1(const Ctx<Tin, Tout>& c, const Levels& lv, int64_t t0,
+                                       float (&out)[8]) {
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
@@ -89,6 +98,7 @@ __device__ __forceinline__ void level1(const Ctx<Tin, Tout>& c, int64_t t0, floa
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (i0 + u < c.p) {
+        if (c.score0) score(c, lv, 0, t0 + i0 + u, v[u]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += v[u][e];
       }
@@ -105,6 +115,10 @@ __device__ __forceinline__ void level2_p4(const Ctx<Tin, Tout>& c, const Levels&
   float v[16][8];
 #pragma unroll
   for (int u = 0; u < 16; ++u) load8(c.x + (t0 + u) * c.row, v[u]);
+  if (c.score0) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) score(c, lv, 0, t0 + u, v[u]);
+  }
   float acc2[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc2[e] = 0.f;
@@ -126,7 +140,7 @@ template <int LVL, typename Tin, typename Tout>
 __device__ __forceinline__ void pool_block(const Ctx<Tin, Tout>& c, const Levels& lv, int64_t t0,
                                            float (&out)[8]) {
   if constexpr (LVL == 1) {
-    level1(c, t0, out);
+    level1(c, lv, t0, out);
   } else if (LVL == 2 && c.p == 4) {
     level2_p4(c, lv, t0, out);
     emit(c, lv, LVL, t0 / lv.pw[LVL], out);
@@ -180,6 +194,7 @@ __global__ __launch_bounds__(256) void pool_score_kernel(Levels lv, const Tin* _
   c.inv_p = 1.0f / static_cast<float>(lv.p);
   c.hd8 = hd8;
   c.writer = (g % hd8) == 0;
+  c.score0 = stream == 1 && lv.direct;
 
   float out[8];
   pool_block<L - 1>(c, lv, tile * T, out);

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Levels lv, int first, in
 
 hipError_t launch_topk(const Levels& lv, const float* scores, int32_t* sel, hipStream_t st) {
   if (lv.L < 2) return hipSuccess;
-  const int first = 1, last = lv.L - 1;  // REFINE selects at levels 1..L-1
+  const int first = lv.sel_first, last = lv.sel_last;  // REFINE: 1..L-1; DIRECT: 0..L-2
   int64_t chunks = 0;
   for (int l = first; l <= last; ++l) chunks += lv.nchunk[l];
   if (chunks == 0) return hipSuccess;

@@ -12,7 +12,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import LH_BF16, LH_F32, LH_SEL_REFINE, LhAttnDesc, LhConfig, LhGathered, LhPlanInfo, check
+from ._lib import LH_BF16, LH_F32, LH_SEL_DIRECT, LH_SEL_REFINE, LhAttnDesc, LhConfig, LhGathered, LhPlanInfo, check
 
 _TORCH_DTYPE = {LH_BF16: torch.bfloat16, LH_F32: torch.float32}
 
@@ -35,7 +35,7 @@ def make_config(batch, n_tokens, heads, head_dim, levels, pool, k, chunk, dtype=
 def config_for(w) -> LhConfig:
     """lh_config of a synth.Workload."""
     return make_config(w.batch, w.n_tokens, w.heads, w.head_dim, w.levels, w.pool, w.k, w.chunk,
-                       w.dtype)
+                       w.dtype, select_mode=LH_SEL_DIRECT if w.mode == "direct" else LH_SEL_REFINE)
 
 
 def torch_dtype(cfg: LhConfig):

@@ -42,6 +42,7 @@ class Workload:
     chunk: int
     seed: int
     backward: bool
+    mode: str = "refine"  # selection reading: "refine" (the contract) or "direct"
 
 
 WORKLOADS = {

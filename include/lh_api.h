@@ -86,11 +86,16 @@ typedef enum lh_status {
   LH_ERR_ALIGN = -8,       /* a device pointer is not 16-byte aligned                      */
   LH_ERR_WORKSPACE = -9,   /* workspace smaller than lh_plan reports                       */
   LH_ERR_LAUNCH = -10,     /* the HIP runtime refused a launch                             */
-  LH_ERR_UNSUPPORTED = -11 /* a valid but unimplemented option (select_mode DIRECT)        */
+  LH_ERR_UNSUPPORTED = -11 /* an unknown select_mode                                       */
 } lh_status;
 
 typedef enum lh_dtype { LH_BF16 = 0, LH_F32 = 1 } lh_dtype;
 
+/* Which entries the selection keeps and how they enter the gathered sequence.  REFINE: k_l
+ * entries are kept at levels 1..L-1 and each enters as its p children one level finer
+ * (S = n_{L-1} + p * sum k_l; the reading that reproduces the pages' ~65K at N = 1e6).
+ * DIRECT: the literal reading -- k_l entries are kept at levels 0..L-2 and enter themselves
+ * (S = n_{L-1} + sum k_l).  In both the coarsest level enters whole. */
 typedef enum lh_select_mode { LH_SEL_REFINE = 0, LH_SEL_DIRECT = 1 } lh_select_mode;
 
 /* Problem statement of one layer call: the pages' N, heads, head_dim, L, p, per-level k and
@@ -102,11 +107,12 @@ typedef struct lh_config {
   int32_t head_dim;       /* D in {64, 128}                                               */
   int32_t levels;         /* L in [1, 8]; L = 1 is dense causal attention (S = N)         */
   int32_t pool;           /* p in [2, 16]                                                 */
-  int32_t k[LH_MAX_LEVELS]; /* REFINE: k[l] = kept entries at level l, l = 1..L-1; k[0]
-                               unused; k[l] >= n_l keeps the whole level                   */
+  int32_t k[LH_MAX_LEVELS]; /* k[l] = kept entries at selected level l (REFINE l = 1..L-1,
+                               DIRECT l = 0..L-2); other entries unused; k[l] >= n_l
+                               keeps the whole level                                     */
   int32_t chunk;          /* C: power of two in [16, 2048]                                */
   int32_t dtype;          /* lh_dtype of Q, K, V, Y, dY, dQ, dK, dV                       */
-  int32_t select_mode;    /* lh_select_mode; only LH_SEL_REFINE is implemented            */
+  int32_t select_mode;    /* lh_select_mode                                               */
   float softmax_scale;    /* <= 0 selects 1/sqrt(D)                                       */
 } lh_config;
 
@@ -150,7 +156,8 @@ const char* lh_status_string(lh_status status);
  *            pooled_offset[l] .. pooled_offset[l] + n_l - 1; each is the mean of p entries of
  *            the level below (float32 arithmetic, one rounding if pooled_dtype is bf16)
  *   scores   device float32 [B, H, pyramid_total], indexed by pyramid id; levels 1..L-1 are
- *            written (level 0 is not scored in REFINE and is left untouched)
+ *            written, and level 0 (the raw key rows) too in DIRECT; REFINE leaves level 0
+ *            untouched
  *   Any of pq/pk/pv may be NULL to skip that stream's pooled output (scores still come
  *   from K).  With L = 1 nothing is launched. */
 lh_status lh_pool_score(const lh_config* cfg, const void* q, const void* k, const void* v,

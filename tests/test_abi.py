@@ -87,10 +87,23 @@ def test_plan_rejects(kw, code):
     assert e.value.name == code
 
 
-def test_direct_mode_is_reported_unsupported():
+def test_unknown_select_mode_is_reported_unsupported():
     with pytest.raises(_lib.LhError) as e:
-        ops.lh_plan(_cfg(select_mode=_lib.LH_SEL_DIRECT))
+        ops.lh_plan(_cfg(select_mode=7))
     assert e.value.name == "LH_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("levels,pool,k,n", [(3, 4, 100, 4096), (4, 2, 64, 2048), (2, 4, 5000, 4096),
+                                             (4, 4, 4096, 524288)])
+def test_plan_direct_closed_forms(levels, pool, k, n):
+    cfg = _cfg(select_mode=_lib.LH_SEL_DIRECT, levels=levels, pool=pool, k=k, n_tokens=n, chunk=64)
+    info = ops.lh_plan(cfg)
+    ocfg = O.Config(levels, pool, k, 64, mode=O.DIRECT)
+    assert info.gathered_len == O.gathered_length(n, ocfg)
+    sizes = O.level_sizes(n, levels, pool)
+    assert info.gathered_len == sizes[-1] + sum(min(k, m) for m in sizes[:-1])
+    assert [info.k_eff[l] for l in range(levels)] == [min(k, m) for m in sizes[:-1]] + [0]
+    assert info.sel_total == sum(min(k, m) for m in sizes[:-1])
 
 
 def _call(name, *args):

@@ -9,6 +9,8 @@ selection, and the gathered map must equal the oracle's order for that selection
 Also checks that the staged runner and lh_forward / lh_backward produce identical bits.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -24,10 +26,17 @@ def f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def workload(name):
+    if name.endswith("-direct"):  # the same inputs under the DIRECT selection reading
+        return dataclasses.replace(synth.WORKLOADS[name[:-len("-direct")]], name=name,
+                                   mode="direct")
+    return synth.WORKLOADS[name]
+
+
 @pytest.mark.parametrize("name,heads", [("layer-98k", (0, 15)), ("lh-512k", (0, 15)),
-                                        ("stress-1m", (7,))])
+                                        ("stress-1m", (7,)), ("lh-512k-direct", (3,))])
 def test_full_size_heads_against_oracle(name, heads):
-    w = synth.WORKLOADS[name]
+    w = workload(name)
     x = synth.workload_inputs(w)
     t = {n: torch.from_numpy(a).to("cuda").to(torch.bfloat16) for n, a in x.items()}
     cfg = ops.config_for(w)
@@ -42,7 +51,9 @@ def test_full_size_heads_against_oracle(name, heads):
         assert torch.equal(a, b)
 
     info = layer.info
-    ocfg = O.Config(w.levels, w.pool, w.k, w.chunk)
+    direct = w.mode == "direct"
+    ocfg = O.Config(w.levels, w.pool, w.k, w.chunk, mode=O.DIRECT if direct else O.REFINE)
+    levels = range(0, w.levels - 1) if direct else range(1, w.levels)
     sel_np = layer.sel.cpu().numpy()
     gmap_np = layer.gmap.cpu().numpy()
     offs = np.array([info.level_offset[l] for l in range(w.levels)])
@@ -51,7 +62,7 @@ def test_full_size_heads_against_oracle(name, heads):
         _, scores, own = O.head_selection(k, ocfg)
         gsel = {}
         swaps = 0
-        for lv in range(1, w.levels):
+        for lv in levels:
             o = info.sel_offset[lv]
             got = sel_np[0, h, o:o + info.k_eff[lv]].astype(np.int64)
             assert np.all(np.diff(got) > 0)

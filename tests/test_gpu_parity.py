@@ -43,7 +43,12 @@ def inputs(w, with_grad=True):
 
 
 def ocfg(w):
-    return O.Config(w.levels, w.pool, w.k, w.chunk)
+    return O.Config(w.levels, w.pool, w.k, w.chunk, mode=O.DIRECT if w.mode == "direct" else O.REFINE)
+
+
+def sel_levels(w):
+    """Levels the selection runs on: 1..L-1 (REFINE) or 0..L-2 (DIRECT)."""
+    return range(0, w.levels - 1) if w.mode == "direct" else range(1, w.levels)
 
 
 def small(name, **kw):
@@ -65,8 +70,12 @@ DENSE = synth.Workload("dense", 1, 640, 2, 64, "bf16", 1, 4, 0, 64, 13, True)
 POOL2 = synth.Workload("pool2-l5", 1, 4096, 2, 64, "bf16", 5, 2, 100, 256, 14, True)
 # a pool factor that is not a power of two (division instead of shifts), three chunks
 POOL3 = synth.Workload("pool3", 1, 4608, 2, 64, "bf16", 3, 3, 100, 512, 15, True)
-STAGE_CASES = [TINY, RAGGED, WIDE, POOL2, POOL3]
-E2E_CASES = [TINY, RAGGED, WIDE, DENSE, POOL2, POOL3]
+# the DIRECT selection reading: kept entries of levels 0..L-2 enter themselves
+DIRECT = synth.Workload("direct", 1, 4096, 2, 64, "bf16", 3, 4, 100, 64, 16, True, "direct")
+DIRECT_P2 = synth.Workload("direct-p2-d128", 1, 2048, 2, 128, "bf16", 4, 2, 64, 128, 17, True,
+                           "direct")
+STAGE_CASES = [TINY, RAGGED, WIDE, POOL2, POOL3, DIRECT, DIRECT_P2]
+E2E_CASES = [TINY, RAGGED, WIDE, DENSE, POOL2, POOL3, DIRECT, DIRECT_P2]
 
 
 def pooled_rows_oracle(x, w):
@@ -102,19 +111,27 @@ def test_pool_score(w):
                         rel = np.abs(s_got - s_ref) / np.maximum(s_ref, 1e-30)
                         worst_rel = max(worst_rel, float(rel.max()))
                         assert np.all(rel <= 1e-4), (b, h, lv)
+    if w.mode == "direct":  # the raw key rows are scored too
+        for b in range(w.batch):
+            for h in range(w.heads):
+                s_ref = np.linalg.norm(x["k"][b, :, h].astype(np.float64), axis=1)
+                s_got = f64(sc[b, h, :w.n_tokens])
+                rel = np.abs(s_got - s_ref) / np.maximum(s_ref, 1e-30)
+                worst_rel = max(worst_rel, float(rel.max()))
+                assert np.all(rel <= 1e-4), (b, h, 0)
     print(f"[{w.name}] worst score relative error {worst_rel:.3e}")
     # bf16 pooled output is the same float32 value rounded once
     pq16, pk16, pv16, sc16 = ops.lh_pool_score(cfg, t["q"], t["k"], t["v"], pooled_dtype=torch.bfloat16)
     for a, b16 in ((pq, pq16), (pk, pk16), (pv, pv16)):
         assert torch.equal(a.to(torch.bfloat16), b16)
-    lo = info.level_offset[1]
+    lo = info.level_offset[min(sel_levels(w), default=1)]
     assert torch.equal(sc[:, :, lo:], sc16[:, :, lo:])
 
 
 # ------------------------------------------------------------------------ stage 3
 def _oracle_select(scores_np, w, info):
     return {lv: O.select_level(scores_np[info.level_offset[lv]:info.level_offset[lv] + info.level_size[lv]],
-                               w.k, w.chunk) for lv in range(1, w.levels)}
+                               w.k, w.chunk) for lv in sel_levels(w)}
 
 
 @pytest.mark.parametrize("w", STAGE_CASES + [MEDIUM], ids=lambda w: w.name)
@@ -129,7 +146,7 @@ def test_topk_exact_on_gpu_scores(w):
     for b in range(w.batch):
         for h in range(w.heads):
             want = _oracle_select(sc_np[b, h], w, info)
-            for lv in range(1, w.levels):
+            for lv in sel_levels(w):
                 o = info.sel_offset[lv]
                 got = sel_np[b, h, o:o + info.k_eff[lv]]
                 assert np.array_equal(got, want[lv]), (b, h, lv)
@@ -146,7 +163,7 @@ def test_topk_against_float64_scores_with_near_ties(w):
     for b in range(w.batch):
         for h in range(w.heads):
             _, scores, want = O.head_selection(x["k"][b, :, h].astype(np.float64), ocfg(w))
-            for lv in range(1, w.levels):
+            for lv in sel_levels(w):
                 o = info.sel_offset[lv]
                 got = set(sel[b, h, o:o + info.k_eff[lv]].tolist())
                 ref = set(want[lv].tolist())
@@ -180,7 +197,7 @@ def test_map_and_gather(w):
     for b in range(w.batch):
         for h in range(w.heads):
             s = {lv: sel_np[b, h, info.sel_offset[lv]:info.sel_offset[lv] + info.k_eff[lv]]
-                 for lv in range(1, w.levels)}
+                 for lv in sel_levels(w)}
             glev, gidx = O.gathered_set(s, sizes, ocfg(w))
             ids = offs[glev] + gidx
             assert np.array_equal(gmap_np[b, h, :S], ids)
