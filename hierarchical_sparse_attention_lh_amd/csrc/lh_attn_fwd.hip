@@ -26,6 +26,9 @@
 //     rescale of the accumulators; the final division by the row sum is exact either way.
 //   * The row sum is a per-tile tree sum added to a Kahan-compensated total: thousands of
 //     small terms otherwise drift by ~1e-4 relative, which the backward's Delta amplifies.
+//   * Software pipeline: the score product of key tile t+1 is issued inside the softmax of
+//     tile t, one MFMA per short group of vector instructions (a SIMD overlaps an MFMA
+//     mostly with the issuing wave's own independent vector work).
 //   * Workgroups are mapped XCD-aware (one contiguous range of heads per XCD), heavy
 //     (diagonal-far) query tiles first.
 #include <type_traits>
@@ -247,8 +250,8 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
   if (hl == 0) lse[bh * Sp + myq] = m_run + log2f(l_tot);  // base-2 log-sum-exp
 }
 
-// D = 64 fits three waves per SIMD (134 VGPRs), so MFMA work of one wave overlaps the
-// softmax arithmetic of the others; D = 128 keeps the compiler's default.
+// D = 64 is held to two waves per SIMD (the pipelined loop needs ~220 VGPRs; more waves would
+// spill); D = 128 keeps the compiler's default.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attn_fwd_d64(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
              const uint16_t* __restrict__ vt, float* __restrict__ o, float* __restrict__ lse,

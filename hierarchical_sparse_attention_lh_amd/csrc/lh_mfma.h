@@ -16,7 +16,6 @@ namespace lh {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -31,18 +30,6 @@ __device__ __forceinline__ bf16x8 ld_op16(const uint16_t* p) {
   return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
 }
 
-// two 8-byte pieces (elements p0[0..3] and p1[0..3]) as one operand
-__device__ __forceinline__ bf16x8 ld_op8x2(const uint16_t* p0, const uint16_t* p1) {
-  const u32x2 a = *reinterpret_cast<const u32x2*>(p0);
-  const u32x2 b = *reinterpret_cast<const u32x2*>(p1);
-  u32x4 u;
-  u.x = a.x;
-  u.y = a.y;
-  u.z = b.x;
-  u.w = b.y;
-  return as_bf16x8(u);
-}
-
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -53,22 +40,12 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// C registers 8*half .. 8*half+7 of one 32x32 tile, rounded to bf16, as a B (or A) operand.
-// For lane l these are rows (half*16) + {0..3, 8..11} + (l/32)*4 of the tile, i.e. the
-// k index (l/32)*8 + ii of the next product maps to tile row
-//   16*half + (ii/4)*8 + (l/32)*4 + (ii%4).
-__device__ __forceinline__ bf16x8 c_to_op(const f32x16& c, int half) {
-  u32x4 u;
-  u.x = pk_bf16(c[8 * half + 0], c[8 * half + 1]);
-  u.y = pk_bf16(c[8 * half + 2], c[8 * half + 3]);
-  u.z = pk_bf16(c[8 * half + 4], c[8 * half + 5]);
-  u.w = pk_bf16(c[8 * half + 6], c[8 * half + 7]);
-  return as_bf16x8(u);
-}
-
-// Split C registers 8*half .. 8*half+7 into two bf16 operands with hi + lo = value to about
-// 16 significant bits: hi is the value truncated to bf16 (exact), lo the remainder
-// (exact in float32) rounded to bf16.  Probabilities and score gradients enter every product
+// C registers 8*half .. 8*half+7 of one 32x32 tile as a B (or A) operand: for lane l these
+// are rows (half*16) + {0..3, 8..11} + (l/32)*4 of the tile, i.e. the k index (l/32)*8 + ii
+// of the next product maps to tile row 16*half + (ii/4)*8 + (l/32)*4 + (ii%4).
+// They are split into two bf16 operands with hi + lo = value to about 16 significant bits:
+// hi is the value truncated to bf16 (exact), lo the remainder (exact in float32) rounded to
+// bf16.  Probabilities and score gradients enter every product
 // as this pair (two MFMAs), so their rounding stays far below the gradients' bf16 output
 // rounding; a single bf16 operand (8 bits) is not accurate enough under cancellation.
 __device__ __forceinline__ void c_to_op2(const f32x16& c, int half, bf16x8& hi, bf16x8& lo) {
@@ -98,7 +75,7 @@ __device__ __forceinline__ f32x16 zero16() {
 // Transposed tensors ([.., D, Sp]) store sequence position s at column swap23(s): bits 2 and 3
 // of s exchanged (an involution).  Within each group of 16 the stored order is
 // 0-3, 8-11, 4-7, 12-15, which is exactly the k order in which a C tile leaves an MFMA as the
-// next product's B operand (see c_to_op): the matching A operand of lane l is then the single
+// next product's B operand (see c_to_op2): the matching A operand of lane l is then the single
 // 16-byte chunk 2*t + (l/32) of the row instead of two 8-byte pieces.
 __host__ __device__ __forceinline__ int64_t swap23(int64_t s) {
   return (s & ~int64_t(12)) | ((s & 4) << 1) | ((s & 8) >> 1);
