@@ -12,6 +12,8 @@ namespace {
 using lh::Levels;
 
 constexpr int64_t kMaxTokens = int64_t(1) << 30;
+// attention length bound: the staging loads address a tile with a 32-bit byte offset
+constexpr int64_t kMaxAttnLen = int64_t(1) << 24;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -105,6 +107,7 @@ lh_status check_config(const lh_config* c, Levels* lv) {
   L.K = soff;
   L.S = S;
   if (L.B * L.H * L.P > (int64_t(1) << 40) || L.P >= (int64_t(1) << 31)) return LH_ERR_SHAPE;
+  if (L.S > kMaxAttnLen) return LH_ERR_SHAPE;
   if (lv) *lv = L;
   return LH_OK;
 }
@@ -188,7 +191,7 @@ inline const char* at(const void* base, size_t off) {
 
 lh_status check_desc(const lh_attn_desc* d) {
   if (d == nullptr) return LH_ERR_NULL;
-  if (d->batch < 1 || d->heads < 1 || d->seq < 1 || d->seq > (int64_t(1) << 30)) return LH_ERR_SHAPE;
+  if (d->batch < 1 || d->heads < 1 || d->seq < 1 || d->seq > kMaxAttnLen) return LH_ERR_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return LH_ERR_DTYPE;
   if (d->batch * d->heads * (lh::padded_len(d->seq) / 128) > 0x7fffffffLL) return LH_ERR_SHAPE;
   return LH_OK;

@@ -42,12 +42,16 @@ __device__ __forceinline__ void attn_bwd_kv_body(
     float* __restrict__ dk, float* __restrict__ dv, int S, int Sp, int64_t BH, float scale,
     float sl2) {
   constexpr int BK = 128, NB = BQ / 32;  // NB blocks of 32 queries per tile
-  __shared__ __attribute__((aligned(16))) uint16_t qs[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t ds_[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t qts[2][D * BQ];
-  __shared__ __attribute__((aligned(16))) uint16_t dts[2][D * BQ];
-  __shared__ __attribute__((aligned(16))) float ls[2][BQ];
-  __shared__ __attribute__((aligned(16))) float dl[2][BQ];
+  // Each buffer is its own LDS object and every use names it statically (the loop below is
+  // unrolled by two): the compiler can then tell that the direct loads filling one buffer do
+  // not alias the reads of the other, and does not make a tile's first LDS read wait for the
+  // next tile's loads.
+  __shared__ __attribute__((aligned(16))) uint16_t qs0[BQ * D], qs1[BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t ds0[BQ * D], ds1[BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t qts0[D * BQ], qts1[D * BQ];
+  __shared__ __attribute__((aligned(16))) uint16_t dts0[D * BQ], dts1[D * BQ];
+  __shared__ __attribute__((aligned(16))) float ls0[BQ], ls1[BQ];
+  __shared__ __attribute__((aligned(16))) float dl0[BQ], dl1[BQ];
 
   const int nkt = Sp / BK;
   const int64_t item = xcd_item(blockIdx.x, BH * nkt);
@@ -84,18 +88,32 @@ __device__ __forceinline__ void attn_bwd_kv_body(
 
   const int qt0 = K0 / BQ;
   const int nqt = (S + BQ - 1) / BQ;
+  // byte offset of logical 16-byte chunk 2j + l/32 in row lq of a swizzled 128-byte-row tile
+  // (swz<64>: the XOR key of row r is (r / 2) % 8, the same for rows lq and 32 + lq)
+  uint32_t loff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    loff[j] = static_cast<uint32_t>(lq * 128 + (((2 * j + hl) ^ ((lq >> 1) & 7)) << 4));
 
-  auto stage = [&](int t, int buf) {
+  auto stage = [&](int t, auto bufc) {
+    constexpr bool B1 = decltype(bufc)::value;
     const int q0 = t * BQ;
-    stage_tile<BQ, D, 256>(qb + static_cast<int64_t>(q0) * D, D, qs[buf], tid);
-    stage_tile<BQ, D, 256>(db_ + static_cast<int64_t>(q0) * D, D, ds_[buf], tid);
-    stage_tile<D, BQ, 256>(qtb + q0, Sp, qts[buf], tid);
-    stage_tile<D, BQ, 256>(dtb + q0, Sp, dts[buf], tid);
-    if (wave == 0 && lane < BQ) stage_f32x64(lb + q0, ls[buf], lane);
-    if (wave == 1 && lane < BQ) stage_f32x64(dlb + q0, dl[buf], lane);
+    stage_tile<BQ, D, 256>(qb + static_cast<int64_t>(q0) * D, D, B1 ? qs1 : qs0, tid);
+    stage_tile<BQ, D, 256>(db_ + static_cast<int64_t>(q0) * D, D, B1 ? ds1 : ds0, tid);
+    stage_tile<D, BQ, 256>(qtb + q0, Sp, B1 ? qts1 : qts0, tid);
+    stage_tile<D, BQ, 256>(dtb + q0, Sp, B1 ? dts1 : dts0, tid);
+    if (wave == 0 && lane < BQ) stage_f32x64(lb + q0, B1 ? ls1 : ls0, lane);
+    if (wave == 1 && lane < BQ) stage_f32x64(dlb + q0, B1 ? dl1 : dl0, lane);
   };
 
-  auto tile = [&](auto masked, int t, int buf) {
+  auto tile = [&](auto masked, int t, auto bufc) {
+    constexpr bool B1 = decltype(bufc)::value;
+    const uint16_t* qsb = B1 ? qs1 : qs0;
+    const uint16_t* dsb = B1 ? ds1 : ds0;
+    const uint16_t* qtsb = B1 ? qts1 : qts0;
+    const uint16_t* dtsb = B1 ? dts1 : dts0;
+    const float* lsb = B1 ? ls1 : ls0;
+    const float* dlb_ = B1 ? dl1 : dl0;
     const int q0 = t * BQ;
     // The C rows of a lane are queries b2*32 + g*8 + (l/32)*4 + [0..3] (g = r/4): four float4
     // reads give a lane its 16 per-row values of lse or Delta in register order.
@@ -105,7 +123,7 @@ __device__ __forceinline__ void attn_bwd_kv_body(
       sacc[b2] = zero16();
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 d4 = *reinterpret_cast<const float4*>(&dl[buf][b2 * 32 + g * 8 + hl * 4]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&dlb_[b2 * 32 + g * 8 + hl * 4]);
         pacc[b2][4 * g] = d4.x;
         pacc[b2][4 * g + 1] = d4.y;
         pacc[b2][4 * g + 2] = d4.z;
@@ -113,8 +131,8 @@ __device__ __forceinline__ void attn_bwd_kv_body(
       }
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        sacc[b2] = mfma32(lds_op<D>(qs[buf], b2 * 32 + lq, 2 * kk + hl), kreg[kk], sacc[b2]);
-        pacc[b2] = mfma32(lds_op<D>(ds_[buf], b2 * 32 + lq, 2 * kk + hl), vreg[kk], pacc[b2]);
+        sacc[b2] = mfma32(lds_op<D>(qsb, b2 * 32 + lq, 2 * kk + hl), kreg[kk], sacc[b2]);
+        pacc[b2] = mfma32(lds_op<D>(dsb, b2 * 32 + lq, 2 * kk + hl), vreg[kk], pacc[b2]);
       }
     }
     // pacc now holds Delta - dP, so p * pacc = -dS (the sign is folded into the final scale)
@@ -123,7 +141,7 @@ __device__ __forceinline__ void attn_bwd_kv_body(
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int qi = b2 * 32 + g * 8 + hl * 4;  // 4 consecutive local queries
-        const float4 l4 = *reinterpret_cast<const float4*>(&ls[buf][qi]);
+        const float4 l4 = *reinterpret_cast<const float4*>(&lsb[qi]);
         const float lv4[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -144,8 +162,8 @@ __device__ __forceinline__ void attn_bwd_kv_body(
       c_to_op2(pacc[t4 >> 1], t4 & 1, sh, sl);
 #pragma unroll
       for (int d2 = 0; d2 < D / 32; ++d2) {
-        const bf16x8 ao = lds_op<BQ>(dts[buf], d2 * 32 + lq, 2 * t4 + hl);
-        const bf16x8 aq = lds_op<BQ>(qts[buf], d2 * 32 + lq, 2 * t4 + hl);
+        const bf16x8 ao = lds_op<BQ>(dtsb, d2 * 32 + lq, 2 * t4 + hl);
+        const bf16x8 aq = lds_op<BQ>(qtsb, d2 * 32 + lq, 2 * t4 + hl);
         dvacc[d2] = mfma32(ao, pl, dvacc[d2]);
         dvacc[d2] = mfma32(ao, ph, dvacc[d2]);
         dkacc[d2] = mfma32(aq, sl, dkacc[d2]);
@@ -154,19 +172,227 @@ __device__ __forceinline__ void attn_bwd_kv_body(
     }
   };
 
-  if (qt0 < nqt) stage(qt0, 0);
-  wait_vmem();
-  __syncthreads();
-  for (int t = qt0; t < nqt; ++t) {
-    const int buf = (t - qt0) & 1;
-    if (t + 1 < nqt) stage(t + 1, buf ^ 1);
+  // The same tile for D = 64 and 64 queries, laid out for the matrix cores: twelve groups of
+  // four MFMAs (A: S and dP of one 32-query block, two k steps; V / K: the dV or dK update
+  // of one 16-query chunk t4), each group carrying vector work whose inputs are complete:
+  //   A00 -          A01 -            A10 b0 b1     A11 p0 d0     V0 p1   K0 d1
+  //   V1 b2 b3       K1 p2 d2         V2 p3         K2 d3         V3 -    K3 -
+  // (b = exp and dS of chunk t4, p / d = hi-lo split of P / dS of chunk t4).  A wave's vector
+  // instructions overlap its own MFMAs far better than another wave's, so the layout is
+  // fixed with scheduling barriers; the LDS operands of each group are read one group ahead.
+  auto tile64 = [&](auto masked, int t, auto bufc) {
+    constexpr bool MASK = decltype(masked)::value;
+    constexpr bool B1 = decltype(bufc)::value;
     const int q0 = t * BQ;
-    if (q0 < kw + 31 || q0 + BQ > S)
-      tile(std::true_type{}, t, buf);
-    else
-      tile(std::false_type{}, t, buf);
+    const uint16_t* qsb = B1 ? qs1 : qs0;
+    const uint16_t* dsb = B1 ? ds1 : ds0;
+    const uint16_t* qtsb = B1 ? qts1 : qts0;
+    const uint16_t* dtsb = B1 ? dts1 : dts0;
+    const float* lsb = B1 ? ls1 : ls0;
+    const float* dlb_ = B1 ? dl1 : dl0;
+    f32x16 sacc[2], pacc[2];
+    bf16x8 op[12][4];
+    float4 lsv[2][4];
+    bf16x8 ph[4], pl[4], sh[4], sl[4];
+    // Every operand row here is 128 bytes (64 bf16): logical chunk 2j + l/32 of row 32m + lq
+    // sits at byte 4096m + loff[j] of its tile.  The copies are opaque to the compiler, so the
+    // address sums stay inside the loop and fold into instruction offsets instead of being
+    // hoisted into dozens of live registers.
+    uint32_t lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[j] = loff[j];
+      asm volatile("" : "+v"(lo[j]));
+    }
+    auto rd = [&](const uint16_t* tile_base, int m, int j) {
+      return ld_op16(reinterpret_cast<const uint16_t*>(
+          reinterpret_cast<const char*>(tile_base) + 4096 * m + lo[j]));
+    };
+    auto load_ops = [&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u < 4) {
+        constexpr int b2 = u >> 1, kh = u & 1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int kk = 2 * kh + j;
+          op[u][2 * j] = rd(qsb, b2, kk);
+          op[u][2 * j + 1] = rd(dsb, b2, kk);
+        }
+      } else {
+        constexpr int c = u - 4, t4 = c >> 1;
+        const uint16_t* src = (c & 1) ? qtsb : dtsb;
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) op[u][d2] = rd(src, d2, t4);
+      }
+    };
+    auto mfma_unit = [&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u < 4) {
+        constexpr int b2 = u >> 1, kh = u & 1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int kk = 2 * kh + j;
+          sacc[b2] = mfma32(op[u][2 * j], kreg[kk], sacc[b2]);
+          pacc[b2] = mfma32(op[u][2 * j + 1], vreg[kk], pacc[b2]);
+        }
+      } else if constexpr (((u - 4) & 1) == 0) {
+        constexpr int t4 = (u - 4) >> 1;
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) dvacc[d2] = mfma32(op[u][d2], pl[t4], dvacc[d2]);
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) dvacc[d2] = mfma32(op[u][d2], ph[t4], dvacc[d2]);
+      } else {
+        constexpr int t4 = (u - 4) >> 1;
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) dkacc[d2] = mfma32(op[u][d2], sl[t4], dkacc[d2]);
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) dkacc[d2] = mfma32(op[u][d2], sh[t4], dkacc[d2]);
+      }
+    };
+    auto load_ls = [&](int b2) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        lsv[b2][g] = *reinterpret_cast<const float4*>(&lsb[b2 * 32 + g * 8 + hl * 4]);
+    };
+    // P = exp2(S sl2 - lse) and p * (Delta - dP) for the 8 C registers of chunk t4
+    auto b_unit = [&](int t4) {
+      const int b2 = t4 >> 1, half = t4 & 1;
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int g = 2 * half + gg;
+        const float lv4[4] = {lsv[b2][g].x, lsv[b2][g].y, lsv[b2][g].z, lsv[b2][g].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = g * 4 + u;
+          float p = __builtin_amdgcn_exp2f(fmaf(sacc[b2][r], sl2, -lv4[u]));
+          if constexpr (MASK) {
+            const int qa = q0 + b2 * 32 + g * 8 + hl * 4 + u;
+            if (qa < mykey || qa >= S) p = 0.f;
+          }
+          sacc[b2][r] = p;
+          pacc[b2][r] = p * pacc[b2][r];
+        }
+      }
+    };
+    auto sp_unit = [&](int t4) { c_to_op2(sacc[t4 >> 1], t4 & 1, ph[t4], pl[t4]); };
+    auto sd_unit = [&](int t4) { c_to_op2(pacc[t4 >> 1], t4 & 1, sh[t4], sl[t4]); };
+    // four {one MFMA, nv vector instructions} groups, then a fence
+    auto layout = [&](auto nvc) {
+      constexpr int nv = decltype(nvc)::value;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using N0 = std::integral_constant<int, 0>;
+    using N6 = std::integral_constant<int, 6>;
+    using N12 = std::integral_constant<int, 12>;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    using I6 = std::integral_constant<int, 6>;
+    using I7 = std::integral_constant<int, 7>;
+    using I8 = std::integral_constant<int, 8>;
+    using I9 = std::integral_constant<int, 9>;
+    using I10 = std::integral_constant<int, 10>;
+    using I11 = std::integral_constant<int, 11>;
+
+    // dP accumulators start at Delta (rows in C-register order), score accumulators at 0;
+    // block 1's seed is read just before its first MFMA group
+    auto seed = [&](int b2) {
+      sacc[b2] = zero16();
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 d4 = *reinterpret_cast<const float4*>(&dlb_[b2 * 32 + g * 8 + hl * 4]);
+        pacc[b2][4 * g] = d4.x;
+        pacc[b2][4 * g + 1] = d4.y;
+        pacc[b2][4 * g + 2] = d4.z;
+        pacc[b2][4 * g + 3] = d4.w;
+      }
+    };
+    seed(0);
+    load_ops(I0{});
+    __builtin_amdgcn_sched_barrier(0);
+    load_ops(I1{});
+    mfma_unit(I0{});
+    layout(N0{});
+    load_ops(I2{});
+    seed(1);
+    load_ls(0);
+    mfma_unit(I1{});
+    layout(N0{});
+    load_ops(I3{});
+    mfma_unit(I2{});
+    b_unit(0);
+    b_unit(1);
+    layout(N12{});
+    load_ops(I4{});
+    mfma_unit(I3{});
+    sp_unit(0);
+    sd_unit(0);
+    layout(N12{});
+    load_ops(I5{});
+    load_ls(1);
+    mfma_unit(I4{});
+    sp_unit(1);
+    layout(N6{});
+    load_ops(I6{});
+    mfma_unit(I5{});
+    sd_unit(1);
+    layout(N6{});
+    load_ops(I7{});
+    mfma_unit(I6{});
+    b_unit(2);
+    b_unit(3);
+    layout(N12{});
+    load_ops(I8{});
+    mfma_unit(I7{});
+    sp_unit(2);
+    sd_unit(2);
+    layout(N12{});
+    load_ops(I9{});
+    mfma_unit(I8{});
+    sp_unit(3);
+    layout(N6{});
+    load_ops(I10{});
+    mfma_unit(I9{});
+    sd_unit(3);
+    layout(N6{});
+    load_ops(I11{});
+    mfma_unit(I10{});
+    layout(N0{});
+    mfma_unit(I11{});
+    layout(N0{});
+  };
+
+  auto step = [&](int t, auto bufc) {
+    if (t + 1 < nqt) stage(t + 1, std::integral_constant<bool, !decltype(bufc)::value>{});
+    const int q0 = t * BQ;
+    if constexpr (D == 64 && BQ == 64) {
+      if (q0 < kw + 31 || q0 + BQ > S)
+        tile64(std::true_type{}, t, bufc);
+      else
+        tile64(std::false_type{}, t, bufc);
+    } else {
+      if (q0 < kw + 31 || q0 + BQ > S)
+        tile(std::true_type{}, t, bufc);
+      else
+        tile(std::false_type{}, t, bufc);
+    }
     wait_vmem();
     __syncthreads();
+  };
+  if (qt0 < nqt) stage(qt0, std::false_type{});
+  wait_vmem();
+  __syncthreads();
+  for (int t = qt0; t < nqt; t += 2) {
+    step(t, std::false_type{});
+    if (t + 1 < nqt) step(t + 1, std::true_type{});
   }
 
   float* dkr = dk + (bh * Sp + mykey) * D;

@@ -103,9 +103,12 @@ __device__ __forceinline__ bf16x8 lds_op(const uint16_t* tile, int row, int chun
 // Stage ROWS x ROW_ELEMS bf16 (row stride `gstride` elements in global memory) into a swizzled
 // LDS tile with gfx950 direct global->LDS loads: each wave instruction moves 64 x 16 bytes into
 // 1 KB of contiguous LDS, so lane l fetches the global chunk that belongs at LDS chunk
-// (instruction base + l).  No VGPRs hold the data; completion is tracked by vmcnt.
+// (instruction base + l).  No VGPRs hold the data; completion is tracked by vmcnt.  The lane's
+// byte offset from the (uniform) tile start is 32-bit, so the loads take the scalar-base +
+// 32-bit-offset form and keep no 64-bit address per lane; callers bound
+// (ROWS - 1) * gstride + ROW_ELEMS below 2^31 elements.
 template <int ROWS, int ROW_ELEMS, int NT>
-__device__ __forceinline__ void stage_tile(const uint16_t* g, int64_t gstride, uint16_t* lds,
+__device__ __forceinline__ void stage_tile(const uint16_t* g, int gstride, uint16_t* lds,
                                            int tid) {
   constexpr int CPR = ROW_ELEMS / 8;        // 16-byte chunks per row
   constexpr int CHUNKS = ROWS * CPR;
@@ -117,13 +120,18 @@ __device__ __forceinline__ void stage_tile(const uint16_t* g, int64_t gstride, u
     const int lin = base + lane;
     const int row = lin / CPR, pc = lin % CPR;
     const int c = swz<ROW_ELEMS>(row, pc);
-    __builtin_amdgcn_global_load_lds(g + row * gstride + c * 8, lds + base * 8, 16, 0, 0);
+    uint32_t boff = static_cast<uint32_t>(row * gstride + c * 8) * 2u;
+    asm volatile("" : "+v"(boff));  // opaque: not re-associated with the tile base and hoisted
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(g) + boff, lds + base * 8, 16,
+                                     0, 0);
   }
 }
 
 // 64 floats into LDS with one wave instruction (4 bytes per lane).
 __device__ __forceinline__ void stage_f32x64(const float* g, float* lds, int lane) {
-  __builtin_amdgcn_global_load_lds(g + lane, lds, 4, 0, 0);
+  uint32_t boff = 4u * lane;
+  asm volatile("" : "+v"(boff));
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(g) + boff, lds, 4, 0, 0);
 }
 
 // Lanes l and l ^ 32 exchange a value with one v_permlane32_swap (no LDS round trip); the

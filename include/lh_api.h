@@ -76,7 +76,8 @@ typedef void* lh_stream_t; /* hipStream_t */
 typedef enum lh_status {
   LH_OK = 0,
   LH_ERR_NULL = -1,        /* a required pointer is NULL                                  */
-  LH_ERR_SHAPE = -2,       /* batch/tokens/heads out of range, or p^(L-1) does not divide N */
+  LH_ERR_SHAPE = -2,       /* batch/tokens/heads out of range, gathered length S above
+                              2^24, or p^(L-1) does not divide N */
   LH_ERR_LEVELS = -3,      /* levels outside [1, LH_MAX_LEVELS]                            */
   LH_ERR_POOL = -4,        /* pool factor outside [2, 16]                                  */
   LH_ERR_K = -5,           /* a budget k[l] < 0                                            */
@@ -202,7 +203,7 @@ lh_status lh_gather(const lh_config* cfg, const void* q, const void* k, const vo
  * "Nous Research introduced Lighthouse Attention ...", section "How Lighthouse Attention
  * Works": the layer wraps ordinary scaled dot-product attention). */
 typedef struct lh_attn_desc {
-  int64_t batch, heads, seq, head_dim; /* B, H, S, D; D in {64, 128}; 1 <= S <= 2^30;
+  int64_t batch, heads, seq, head_dim; /* B, H, S, D; D in {64, 128}; 1 <= S <= 2^24;
                                           tensors hold Sp = S rounded up to 128 slots      */
   float scale;                         /* <= 0 selects 1/sqrt(D)                        */
 } lh_attn_desc;

@@ -80,6 +80,8 @@ def _cfg(**kw):
     (dict(chunk=8), "LH_ERR_CHUNK"),
     (dict(chunk=4096), "LH_ERR_CHUNK"),
     (dict(n_tokens=12288, levels=2, chunk=2048), "LH_ERR_CHUNK"),  # level 1: 3072 entries
+    # gathered length S = N + 1 above 2^24 (dense attention over every token, L = 1)
+    (dict(n_tokens=2**24 + 1, levels=1, k=0), "LH_ERR_SHAPE"),
 ])
 def test_plan_rejects(kw, code):
     with pytest.raises(_lib.LhError) as e:
@@ -132,6 +134,10 @@ def test_entry_points_reject_bad_pointers_before_launch():
     assert _call("lh_attn_fwd", dd, ok, ok, ok, ok, bad, st) == L["LH_ERR_ALIGN"]
     d2 = _lib.LhAttnDesc(1, 1, 0, 64, 0.0)
     assert _call("lh_attn_fwd", ctypes.byref(d2), ok, ok, ok, ok, ok, st) == L["LH_ERR_SHAPE"]
+    d4 = _lib.LhAttnDesc(1, 1, 2**24 + 1, 64, 0.0)  # above the attention length bound
+    assert _call("lh_attn_fwd", ctypes.byref(d4), ok, ok, ok, ok, ok, st) == L["LH_ERR_SHAPE"]
+    d5 = _lib.LhAttnDesc(1, 1, 2**24, 64, 0.0)      # at the bound: reaches the pointer checks
+    assert _call("lh_attn_fwd", ctypes.byref(d5), ok, ok, ok, ok, bad, st) == L["LH_ERR_ALIGN"]
     d3 = _lib.LhAttnDesc(1, 1, 10, 32, 0.0)
     assert _call("lh_attn_fwd", ctypes.byref(d3), ok, ok, ok, ok, ok, st) == L["LH_ERR_DTYPE"]
     args = [dd] + [ok] * 12 + [st]
