@@ -177,8 +177,9 @@ __device__ __forceinline__ void attn_bwd_kv_body(
   // of one 16-query chunk t4), each group carrying vector work whose inputs are complete:
   //   A00 -          A01 -            A10 b0 b1     A11 p0 d0     V0 p1   K0 d1
   //   V1 b2 b3       K1 p2 d2         V2 p3         K2 d3         V3 -    K3 -
-  // (b = exp and dS of chunk t4, p / d = hi-lo split of P / dS of chunk t4).  A wave's vector
-  // instructions overlap its own MFMAs far better than another wave's, so the layout is
+  // (b = exp and dS of chunk t4, p / d = hi-lo split of P / dS of chunk t4).  A SIMD runs
+  // one wave's vector instructions beside the other wave's MFMAs when both carry an even mix,
+  // while vector work bunched between MFMA runs leaves the matrix core idle, so the layout is
   // fixed with scheduling barriers; the LDS operands of each group are read one group ahead.
   auto tile64 = [&](auto masked, int t, auto bufc) {
     constexpr bool MASK = decltype(masked)::value;

@@ -27,8 +27,9 @@
 //   * The row sum is a per-tile tree sum added to a Kahan-compensated total: thousands of
 //     small terms otherwise drift by ~1e-4 relative, which the backward's Delta amplifies.
 //   * Software pipeline: the score product of key tile t+1 is issued inside the softmax of
-//     tile t, one MFMA per short group of vector instructions (a SIMD overlaps an MFMA
-//     mostly with the issuing wave's own independent vector work).
+//     tile t, one MFMA per short group of vector instructions, so each wave offers the SIMD
+//     an even mix (one wave's vector work runs beside the other wave's MFMAs; bunched vector
+//     work leaves the matrix core idle).
 //   * Workgroups are mapped XCD-aware (one contiguous range of heads per XCD), heavy
 //     (diagonal-far) query tiles first.
 #include <type_traits>
@@ -101,10 +102,10 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
   };
 
   // Online softmax of score tile t and its P V^T product, with the score product of tile t+1
-  // (into nxt, from K buffer !odd) woven into the same instruction stream.  While an MFMA
-  // occupies a SIMD's matrix core, the vector instructions that overlap it come from the
-  // issuing wave, so the code is laid out as short chunks of one MFMA plus the vector work
-  // that can run behind it, and sched_barrier keeps the compiler from regrouping them.
+  // (into nxt, from K buffer !odd) woven into the same instruction stream.  The SIMD overlaps
+  // one wave's vector instructions with the other wave's MFMAs best when neither stream
+  // bunches, so the code is laid out as short chunks of one MFMA plus some vector work, and
+  // sched_barrier keeps the compiler from regrouping them.
   auto soft_pv = [&](auto masked, int t, f32x16 (&sacc)[2], f32x16 (&nxt)[2], auto par) {
     constexpr bool odd = decltype(par)::value;
     const uint16_t* vsb = odd ? vs1 : vs0;
