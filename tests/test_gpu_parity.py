@@ -74,8 +74,13 @@ POOL3 = synth.Workload("pool3", 1, 4608, 2, 64, "bf16", 3, 3, 100, 512, 15, True
 DIRECT = synth.Workload("direct", 1, 4096, 2, 64, "bf16", 3, 4, 100, 64, 16, True, "direct")
 DIRECT_P2 = synth.Workload("direct-p2-d128", 1, 2048, 2, 128, "bf16", 4, 2, 64, 128, 17, True,
                            "direct")
-STAGE_CASES = [TINY, RAGGED, WIDE, POOL2, POOL3, DIRECT, DIRECT_P2]
-E2E_CASES = [TINY, RAGGED, WIDE, DENSE, POOL2, POOL3, DIRECT, DIRECT_P2]
+# degenerate budgets: nothing selected (only the coarsest level is gathered, S = n_{L-1} = 128,
+# the first 15 tokens receive nothing) and everything selected (k >= n_l at every level: the
+# whole pyramid is gathered, S = 1024 + 256 + 64; level 2 is a single chunk of exactly C)
+EMPTY_SEL = synth.Workload("empty-sel", 1, 2048, 2, 64, "bf16", 3, 4, 0, 64, 18, True)
+FULL_BUDGET = synth.Workload("full-budget", 1, 1024, 2, 64, "bf16", 3, 4, 1000, 64, 19, True)
+STAGE_CASES = [TINY, RAGGED, WIDE, POOL2, POOL3, DIRECT, DIRECT_P2, EMPTY_SEL, FULL_BUDGET]
+E2E_CASES = [TINY, RAGGED, WIDE, DENSE, POOL2, POOL3, DIRECT, DIRECT_P2, EMPTY_SEL, FULL_BUDGET]
 
 
 def pooled_rows_oracle(x, w):
