@@ -26,10 +26,11 @@
 //     rescale of the accumulators; the final division by the row sum is exact either way.
 //   * The row sum is a per-tile tree sum added to a Kahan-compensated total: thousands of
 //     small terms otherwise drift by ~1e-4 relative, which the backward's Delta amplifies.
-//   * Software pipeline: the score product of key tile t+1 is issued inside the softmax of
-//     tile t, one MFMA per short group of vector instructions, so each wave offers the SIMD
-//     an even mix (one wave's vector work runs beside the other wave's MFMAs; bunched vector
-//     work leaves the matrix core idle).
+//   * Software pipeline (D = 64): the score product of key tile t+1 is issued inside the
+//     softmax of tile t, one MFMA per short group of vector instructions, so each wave offers
+//     the SIMD an even mix (one wave's vector work runs beside the other wave's MFMAs;
+//     bunched vector work leaves the matrix core idle).  At D = 128 the pipeline's registers
+//     would force one wave per SIMD, and the plain loop at two waves is faster.
 //   * Workgroups are mapped XCD-aware (one contiguous range of heads per XCD), heavy
 //     (diagonal-far) query tiles first.
 #include <type_traits>
@@ -43,7 +44,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 8.0f;  // base-2 growth of the row max tolerated before a rescale
 
-template <int D>
+template <int D, bool PIPE>
 __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
                                               const uint16_t* __restrict__ k,
                                               const uint16_t* __restrict__ vt,
@@ -223,17 +224,113 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
     __syncthreads();
   };
 
-  f32x16 sa[2], sb[2];
-  stage_k(0, std::false_type{});
-  stage_v(0, std::false_type{});
-  if (nkt > 1) stage_k(1, std::true_type{});
-  wait_vmem();
-  __syncthreads();
-  scores(sa, std::false_type{});
-  __syncthreads();  // K(0)'s buffer is refilled by the first step
-  for (int t = 0; t < nkt; t += 2) {
-    step(t, sa, sb, std::false_type{});
-    if (t + 1 < nkt) step(t + 1, sb, sa, std::true_type{});
+  // Without the pipeline (D = 128): one key tile is S^T = K Q^T (two 32-key C blocks), the
+  // online softmax, O^T += V^T P^T; two waves share each SIMD and one wave's softmax runs
+  // beside the other's MFMAs.
+  auto plain_tile = [&](auto masked, int t, auto bufc) {
+    constexpr bool B1 = decltype(bufc)::value;
+    const uint16_t* ksb = B1 ? ks1 : ks0;
+    const uint16_t* vsb = B1 ? vs1 : vs0;
+    f32x16 sacc[2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) sacc[b2] = zero16();
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+        sacc[b2] = mfma32(lds_op<D>(ksb, b2 * 32 + lq, 2 * kk + hl), qreg[kk], sacc[b2]);
+    if constexpr (decltype(masked)::value) {
+      const int k0 = t * BN;
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + b2 * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+          if (key > myq || key >= S) sacc[b2][r] = -INFINITY;
+        }
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[b2][r]);
+    mx = pair_max(mx) * sl2;
+    const bool grow = mx > m_run + kSlack;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      l_run *= alpha;
+      l_cmp *= alpha;
+      m_run = m_new;
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sacc[b2][r] = __builtin_amdgcn_exp2f(fmaf(sacc[b2][r], sl2, -m_run));
+    float part[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[r] = sacc[0][r] + sacc[1][r];
+#pragma unroll
+    for (int w2 = 8; w2 >= 1; w2 >>= 1)
+#pragma unroll
+      for (int r = 0; r < w2; ++r) part[r] += part[r + w2];
+    const float yk = part[0] - l_cmp;
+    const float tk = l_run + yk;
+    l_cmp = (tk - l_run) - yk;
+    l_run = tk;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      bf16x8 ph, pl;
+      c_to_op2(sacc[t4 >> 1], t4 & 1, ph, pl);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 a = lds_op<BN>(vsb, db * 32 + lq, 2 * t4 + hl);
+        oacc[db] = mfma32(a, pl, oacc[db]);
+        oacc[db] = mfma32(a, ph, oacc[db]);
+      }
+    }
+  };
+
+  auto plain_step = [&](int t, auto bufc) {
+    if (t + 1 < nkt) {
+      stage_k(t + 1, std::integral_constant<bool, !decltype(bufc)::value>{});
+      stage_v(t + 1, std::integral_constant<bool, !decltype(bufc)::value>{});
+    }
+    const int k0 = t * BN;
+    if (k0 + BN - 1 > qw || k0 + BN > S)
+      plain_tile(std::true_type{}, t, bufc);
+    else
+      plain_tile(std::false_type{}, t, bufc);
+    wait_vmem();
+    __syncthreads();
+  };
+  if constexpr (PIPE) {
+    f32x16 sa[2], sb[2];
+    stage_k(0, std::false_type{});
+    stage_v(0, std::false_type{});
+    if (nkt > 1) stage_k(1, std::true_type{});
+    wait_vmem();
+    __syncthreads();
+    scores(sa, std::false_type{});
+    __syncthreads();  // K(0)'s buffer is refilled by the first step
+    for (int t = 0; t < nkt; t += 2) {
+      step(t, sa, sb, std::false_type{});
+      if (t + 1 < nkt) step(t + 1, sb, sa, std::true_type{});
+    }
+  } else {
+    stage_k(0, std::false_type{});
+    stage_v(0, std::false_type{});
+    wait_vmem();
+    __syncthreads();
+    for (int t = 0; t < nkt; t += 2) {
+      plain_step(t, std::false_type{});
+      if (t + 1 < nkt) plain_step(t + 1, std::true_type{});
+    }
   }
 
   const float l_own = l_run - l_cmp;
@@ -251,22 +348,21 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ q,
   if (hl == 0) lse[bh * Sp + myq] = m_run + log2f(l_tot);  // base-2 log-sum-exp
 }
 
-// D = 64 is held to two waves per SIMD (the pipelined loop needs ~220 VGPRs; more waves would
-// spill); D = 128 keeps the compiler's default.
+// Both run two waves per SIMD.  D = 64 uses the pipelined loop (~210 VGPRs); at D = 128 the
+// pipelined loop would spill at two waves and runs 18 % slower at one, so D = 128 uses the
+// plain loop (253 VGPRs).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attn_fwd_d64(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
              const uint16_t* __restrict__ vt, float* __restrict__ o, float* __restrict__ lse,
              int S, int Sp, int64_t BH, float sl2) {
-  attn_fwd_body<64>(q, k, vt, o, lse, S, Sp, BH, sl2);
+  attn_fwd_body<64, true>(q, k, vt, o, lse, S, Sp, BH, sl2);
 }
 
-__global__ __launch_bounds__(256) void attn_fwd_d128(const uint16_t* __restrict__ q,
-                                                     const uint16_t* __restrict__ k,
-                                                     const uint16_t* __restrict__ vt,
-                                                     float* __restrict__ o,
-                                                     float* __restrict__ lse, int S, int Sp,
-                                                     int64_t BH, float sl2) {
-  attn_fwd_body<128>(q, k, vt, o, lse, S, Sp, BH, sl2);
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+attn_fwd_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+              const uint16_t* __restrict__ vt, float* __restrict__ o, float* __restrict__ lse,
+              int S, int Sp, int64_t BH, float sl2) {
+  attn_fwd_body<128, false>(q, k, vt, o, lse, S, Sp, BH, sl2);
 }
 
 }  // namespace
