@@ -14,8 +14,9 @@
 //     the diagonal down.  S = Q K^T and dP = dO V^T are computed with keys as the C column,
 //     so P and dS leave the C registers as B operands of dV^T = dO^T P and dK^T = Q^T dS;
 //     Q^T and dO^T come pre-transposed in the swap23 order those operands need.
-//   * query pass (dQ): workgroup = 128 queries (4 waves x 32), the forward's layout:
-//     S^T = K Q^T, dP^T = V dO^T, dS^T feeds dQ^T = K^T dS^T as the B operand.
+//   * query pass (dQ): workgroup = 128 queries (4 waves x 32), the forward's layout, over
+//     64-key tiles (32 at D = 128): S^T = K Q^T, dP^T = V dO^T, dS^T feeds dQ^T = K^T dS^T
+//     as the B operand.
 // The query pass recomputes S and dP (two extra products) instead of accumulating dQ with
 // atomics across key workgroups; the result is bitwise reproducible.  Tiles are staged with
 // direct global->LDS loads into XOR-swizzled rows (double-buffered); only diagonal and
@@ -415,14 +416,14 @@ __device__ __forceinline__ void attn_bwd_kv_body(
 }
 
 // -------------------------------------------------------------------------- query pass
-template <int D>
+template <int D, int BN>
 __device__ __forceinline__ void attn_bwd_q_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ kt,
     const float* __restrict__ lse, const float* __restrict__ delta,
     const uint16_t* __restrict__ dout, float* __restrict__ dq, int S, int Sp, int64_t BH,
     float scale, float sl2) {
-  constexpr int BM = 128, BN = 64;
+  constexpr int BM = 128, NBK = BN / 32;  // NBK blocks of 32 keys per tile
   __shared__ __attribute__((aligned(16))) uint16_t ks0[BN * D], ks1[BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t vs0[BN * D], vs1[BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t kts0[D * BN], kts1[D * BN];
@@ -456,6 +457,13 @@ __device__ __forceinline__ void attn_bwd_q_body(
 
   const int kend = S < Q0 + BM ? S : Q0 + BM;
   const int nkt = (kend + BN - 1) / BN;
+  // per-lane operand offsets: K / V rows (D elements) for k step kk, K^T rows (BN elements)
+  // for 16-key chunk t4; row block m adds 64 * row length * m bytes
+  uint32_t koff[D / 16], toff[BN / 16];
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) koff[j] = lane_chunk_off<D>(lq, hl, j);
+#pragma unroll
+  for (int j = 0; j < BN / 16; ++j) toff[j] = lane_chunk_off<BN>(lq, hl, j);
 
   auto stage = [&](int t, auto bufc) {
     constexpr bool B1 = decltype(bufc)::value;
@@ -471,19 +479,32 @@ __device__ __forceinline__ void attn_bwd_q_body(
     const uint16_t* vsb = B1 ? vs1 : vs0;
     const uint16_t* ktsb = B1 ? kts1 : kts0;
     const int k0 = t * BN;
-    f32x16 sacc[2], pacc[2];
+    // opaque copies: the address sums stay in the loop and fold into instruction offsets
+    // instead of being hoisted into one live register per read
+    uint32_t ko[D / 16], to[BN / 16];
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) {
+    for (int j = 0; j < D / 16; ++j) {
+      ko[j] = koff[j];
+      asm volatile("" : "+v"(ko[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < BN / 16; ++j) {
+      to[j] = toff[j];
+      asm volatile("" : "+v"(to[j]));
+    }
+    f32x16 sacc[NBK], pacc[NBK];
+#pragma unroll
+    for (int b2 = 0; b2 < NBK; ++b2) {
       sacc[b2] = zero16();
       pacc[b2] = zero16();
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        sacc[b2] = mfma32(lds_op<D>(ksb, b2 * 32 + lq, 2 * kk + hl), qreg[kk], sacc[b2]);
-        pacc[b2] = mfma32(lds_op<D>(vsb, b2 * 32 + lq, 2 * kk + hl), oreg[kk], pacc[b2]);
+        sacc[b2] = mfma32(lds_at(ksb, b2 * 64 * D + ko[kk]), qreg[kk], sacc[b2]);
+        pacc[b2] = mfma32(lds_at(vsb, b2 * 64 * D + ko[kk]), oreg[kk], pacc[b2]);
       }
     }
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
+    for (int b2 = 0; b2 < NBK; ++b2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = __builtin_amdgcn_exp2f(fmaf(sacc[b2][r], sl2, -l2));
@@ -494,12 +515,12 @@ __device__ __forceinline__ void attn_bwd_q_body(
         pacc[b2][r] = p * (pacc[b2][r] - dlt);
       }
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
+    for (int t4 = 0; t4 < 2 * NBK; ++t4) {
       bf16x8 sh, sl;
       c_to_op2(pacc[t4 >> 1], t4 & 1, sh, sl);
 #pragma unroll
       for (int d2 = 0; d2 < D / 32; ++d2) {
-        const bf16x8 a = lds_op<BN>(ktsb, d2 * 32 + lq, 2 * t4 + hl);
+        const bf16x8 a = lds_at(ktsb, d2 * 64 * BN + to[t4]);
         dqacc[d2] = mfma32(a, sl, dqacc[d2]);
         dqacc[d2] = mfma32(a, sh, dqacc[d2]);
       }
@@ -537,9 +558,10 @@ __device__ __forceinline__ void attn_bwd_q_body(
     }
 }
 
-
-// D = 64 fits two waves per SIMD in both passes (no AGPR shuffling, no spills); D = 128
-// keeps the compiler's default.
+// Occupancy: at D = 64 both passes run two waves per SIMD (no AGPR traffic, no spills).  At
+// D = 128 the query pass fits two waves with 32-key tiles (236 VGPRs; 8 % faster than 64-key
+// tiles at one wave), while the key pass (128 accumulator and 64 K/V registers per lane)
+// keeps one wave with AGPR accumulators.
 #define LH_KV_ARGS                                                                          \
   const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,                          \
       const uint16_t *__restrict__ v, const uint16_t *__restrict__ qt,                     \
@@ -565,10 +587,11 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_d128(LH_KV_ARGS) {
 }
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attn_bwd_q_d64(LH_Q_ARGS) {
-  attn_bwd_q_body<64>(q, k, v, kt, lse, delta, dout, dq, S, Sp, BH, scale, sl2);
+  attn_bwd_q_body<64, 64>(q, k, v, kt, lse, delta, dout, dq, S, Sp, BH, scale, sl2);
 }
-__global__ __launch_bounds__(256) void attn_bwd_q_d128(LH_Q_ARGS) {
-  attn_bwd_q_body<128>(q, k, v, kt, lse, delta, dout, dq, S, Sp, BH, scale, sl2);
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+attn_bwd_q_d128(LH_Q_ARGS) {
+  attn_bwd_q_body<128, 32>(q, k, v, kt, lse, delta, dout, dq, S, Sp, BH, scale, sl2);
 }
 #undef LH_KV_ARGS
 #undef LH_Q_ARGS

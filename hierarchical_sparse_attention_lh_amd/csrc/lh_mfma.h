@@ -100,6 +100,23 @@ __device__ __forceinline__ bf16x8 lds_op(const uint16_t* tile, int row, int chun
   return ld_op16(tile + row * ROW_ELEMS + (swz<ROW_ELEMS>(row, chunk) << 3));
 }
 
+// Byte offset of logical chunk 2j + l/32 in row lq of a swizzled tile of ROW_ELEMS bf16 per
+// row.  Row 32m + lq has row lq's XOR key (checked below), so its chunk sits
+// 64 * ROW_ELEMS * m bytes further: one per-lane offset per k step serves every 32-row block
+// of every tile of that shape, and the rest of the address is an instruction immediate.
+template <int ROW_ELEMS>
+__device__ __forceinline__ uint32_t lane_chunk_off(int lq, int hl, int j) {
+  constexpr int CPR = ROW_ELEMS / 8, RPL = CPR >= 16 ? 1 : 16 / CPR;  // as in swz
+  static_assert((32 / RPL) % CPR == 0, "rows lq and 32m + lq must share the XOR key");
+  return static_cast<uint32_t>(lq * ROW_ELEMS * 2 + (swz<ROW_ELEMS>(lq, 2 * j + hl) << 4));
+}
+
+// 16-byte MFMA operand at a byte offset into an LDS tile.
+__device__ __forceinline__ bf16x8 lds_at(const uint16_t* tile, uint32_t byte_off) {
+  return ld_op16(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(tile) +
+                                                   byte_off));
+}
+
 // Stage ROWS x ROW_ELEMS bf16 (row stride `gstride` elements in global memory) into a swizzled
 // LDS tile with gfx950 direct global->LDS loads: each wave instruction moves 64 x 16 bytes into
 // 1 KB of contiguous LDS, so lane l fetches the global chunk that belongs at LDS chunk
