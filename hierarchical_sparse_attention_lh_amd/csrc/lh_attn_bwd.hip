@@ -89,12 +89,10 @@ __device__ __forceinline__ void attn_bwd_kv_body(
 
   const int qt0 = K0 / BQ;
   const int nqt = (S + BQ - 1) / BQ;
-  // byte offset of logical 16-byte chunk 2j + l/32 in row lq of a swizzled 128-byte-row tile
-  // (swz<64>: the XOR key of row r is (r / 2) % 8, the same for rows lq and 32 + lq)
+  // per-lane operand offsets of the D = 64 tile (every operand row there holds 64 bf16)
   uint32_t loff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    loff[j] = static_cast<uint32_t>(lq * 128 + (((2 * j + hl) ^ ((lq >> 1) & 7)) << 4));
+  for (int j = 0; j < 4; ++j) loff[j] = lane_chunk_off<64>(lq, hl, j);
 
   auto stage = [&](int t, auto bufc) {
     constexpr bool B1 = decltype(bufc)::value;
@@ -196,10 +194,10 @@ __device__ __forceinline__ void attn_bwd_kv_body(
     bf16x8 op[12][4];
     float4 lsv[2][4];
     bf16x8 ph[4], pl[4], sh[4], sl[4];
-    // Every operand row here is 128 bytes (64 bf16): logical chunk 2j + l/32 of row 32m + lq
-    // sits at byte 4096m + loff[j] of its tile.  The copies are opaque to the compiler, so the
-    // address sums stay inside the loop and fold into instruction offsets instead of being
-    // hoisted into dozens of live registers.
+    // Every operand row here holds 64 bf16, so logical chunk 2j + l/32 of row 32m + lq sits at
+    // byte 4096m + loff[j] of its tile.  The copies are opaque to the compiler, so the address
+    // sums stay inside the loop and fold into instruction offsets instead of being hoisted
+    // into dozens of live registers.
     uint32_t lo[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -207,8 +205,7 @@ __device__ __forceinline__ void attn_bwd_kv_body(
       asm volatile("" : "+v"(lo[j]));
     }
     auto rd = [&](const uint16_t* tile_base, int m, int j) {
-      return ld_op16(reinterpret_cast<const uint16_t*>(
-          reinterpret_cast<const char*>(tile_base) + 4096 * m + lo[j]));
+      return lds_at(tile_base, 4096 * m + lo[j]);
     };
     auto load_ops = [&](auto uc) {
       constexpr int u = decltype(uc)::value;
