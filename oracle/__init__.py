@@ -6,4 +6,4 @@ with the HIP path and imports nothing from it.
 """
 
 from .lighthouse import *  # noqa: F401,F403
-from .lighthouse import Config, REFINE, DIRECT  # noqa: F401
+from .lighthouse import Config, REFINE, DIRECT, SCORERS  # noqa: F401

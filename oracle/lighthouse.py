@@ -29,7 +29,10 @@ Pages cited (titles as published; sections by their headings):
 Readings of what the pages leave open (each is restated where it is used):
   R1 levels l = 0..L-1, level 0 = the raw tokens, n_l = N / p**l, p**(L-1) must divide N.
   R2 pooling = non-overlapping mean of p consecutive entries of the level below.
-  R3 score = l2 norm of the pooled KEY row of one head.
+  R3 score = l2 norm of the pooled KEY row of one head (scorer "k").  The pages name a
+     per-head l2-norm (projection-norm) scorer without naming the vector; two further readings
+     are kept as options: "qk" = ||q_bar|| * ||k_bar|| and "qkv" = the l2 norm of the
+     concatenated row [q_bar; k_bar; v_bar].
   R4 REFINE selection: at levels l = 1..L-1 keep k_l = min(k[l], n_l) entries; each kept
      entry enters the gathered sequence as its p children one level finer; the coarsest
      level enters whole.  S = n_{L-1} + p * sum_l k_l (reproduces the pages' ~65K at
@@ -58,6 +61,7 @@ import numpy as np
 
 REFINE = "refine"
 DIRECT = "direct"
+SCORERS = ("k", "qk", "qkv")
 
 
 # --------------------------------------------------------------------------------------
@@ -78,6 +82,7 @@ class Config:
     mode: str = REFINE
     scale: float | None = None  # None -> 1/sqrt(D)   (reading R8)
     bf16_attention: bool = True  # reading R10
+    scorer: str = "k"  # reading R3: "k", "qk" or "qkv"
     k_list: list = field(init=False)
 
     def __post_init__(self):
@@ -91,6 +96,8 @@ class Config:
             raise ValueError("need L >= 1, p >= 2, chunk >= 1")
         if self.mode not in (REFINE, DIRECT):
             raise ValueError("mode must be refine or direct")
+        if self.scorer not in SCORERS:
+            raise ValueError(f"scorer must be one of {SCORERS}")
 
 
 def level_sizes(n_tokens: int, levels: int, pool: int) -> list:
@@ -162,11 +169,31 @@ def pool_pyramid(x: np.ndarray, levels: int, pool: int) -> list:
 
 
 # --------------------------------------------------------------------------------------
-# stage 2: parameter-free per-head l2 score   ([EN] four-stage section; [CB] "Four-Stage")
+# stage 2: parameter-free per-head l2 score   ([EN] four-stage section; [CB] "Four-Stage"
+#          and "The Bottom Line" for the projection-norm scorer of the recommended recipe)
 # --------------------------------------------------------------------------------------
-def score_pyramid(k_levels: list) -> list:
-    """Score of each pooled key row: its l2 norm (reading R3)."""
-    return [np.sqrt(np.sum(kl * kl, axis=1)) for kl in k_levels]
+def row_norms(levels: list) -> list:
+    """l2 norm of every row of every level."""
+    return [np.sqrt(np.sum(x * x, axis=1)) for x in levels]
+
+
+def score_pyramid(k_levels: list, scorer: str = "k", q_levels=None, v_levels=None) -> list:
+    """Score of each pooled entry of one head (reading R3).
+
+    "k":   ||k_bar||, the norm of the pooled key row;
+    "qk":  ||q_bar|| * ||k_bar||;
+    "qkv": ||[q_bar; k_bar; v_bar]|| = sqrt(||q_bar||^2 + ||k_bar||^2 + ||v_bar||^2).
+    """
+    nk = row_norms(k_levels)
+    if scorer == "k":
+        return nk
+    nq = row_norms(q_levels)
+    if scorer == "qk":
+        return [a * b for a, b in zip(nq, nk)]
+    if scorer == "qkv":
+        nv = row_norms(v_levels)
+        return [np.sqrt(a * a + b * b + c * c) for a, b, c in zip(nq, nk, nv)]
+    raise ValueError(f"unknown scorer {scorer}")
 
 
 # --------------------------------------------------------------------------------------
@@ -371,12 +398,14 @@ class HeadState:
     scale: float
 
 
-def head_selection(k: np.ndarray, cfg: Config, sizes=None):
-    """Pool the keys, score them and select (stages 1-3 for the key stream only)."""
+def head_selection(k: np.ndarray, cfg: Config, sizes=None, q=None, v=None):
+    """Pool, score and select (stages 1-3); q and v are needed by the "qk"/"qkv" scorers."""
     n = k.shape[0]
     sizes = sizes or level_sizes(n, cfg.levels, cfg.pool)
     k_levels = pool_pyramid(k, cfg.levels, cfg.pool)
-    scores = score_pyramid(k_levels)
+    q_levels = pool_pyramid(q, cfg.levels, cfg.pool) if cfg.scorer != "k" else None
+    v_levels = pool_pyramid(v, cfg.levels, cfg.pool) if cfg.scorer == "qkv" else None
+    scores = score_pyramid(k_levels, cfg.scorer, q_levels, v_levels)
     sel = {lv: select_level(scores[lv], cfg.k_list[lv], cfg.chunk) for lv in selected_levels(cfg)}
     return k_levels, scores, sel
 
@@ -391,7 +420,7 @@ def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, cfg: Config, sel=N
     sizes = level_sizes(n, cfg.levels, cfg.pool)
     q_levels = pool_pyramid(q, cfg.levels, cfg.pool)
     v_levels = pool_pyramid(v, cfg.levels, cfg.pool)
-    k_levels, scores, own_sel = head_selection(k, cfg, sizes)
+    k_levels, scores, own_sel = head_selection(k, cfg, sizes, q=q, v=v)
     sel = own_sel if sel is None else {lv: np.asarray(sel[lv], np.int64) for lv in own_sel}
     glev, gidx = gathered_set(sel, sizes, cfg)
     inv = inverse_map(glev, gidx, sizes)

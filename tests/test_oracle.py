@@ -453,3 +453,149 @@ def test_given_selection_reproduces_own_selection(rng):
              for lv, s in st0.sel.items()}
     y2, st2 = O.head_forward(x["q"], x["k"], x["v"], cfg, sel=other)
     assert len(st2.glev) == len(st0.glev) and not np.array_equal(y2, y0)
+
+
+# ---------------------------------------------------------------- DIRECT selection reading
+# DIRECT is the literal reading of the pages' selector: k entries are kept at levels 0..L-2
+# and enter the gathered sequence themselves; the coarsest level enters whole.  Each pin
+# below fails if the selected levels are shifted to 1..L-1.
+def test_direct_length_separates_level_ranges():
+    # N = 4096, L = 3, p = 4, k = 512: levels 0, 1 keep 512 + 512 (S = 256 + 1024 = 1280);
+    # levels 1, 2 would keep 512 + 256 (S = 1024).
+    cfg = _cfg(3, 4, 512, 64, mode=O.DIRECT)
+    assert O.selected_levels(cfg) == [0, 1]
+    sizes, sel, glev, gidx = _random_state(4096, cfg)
+    assert sorted(sel) == [0, 1]
+    assert len(glev) == O.gathered_length(4096, cfg) == 1280
+    assert np.bincount(glev, minlength=3).tolist() == [512, 512, 256]
+
+
+def test_direct_worked_example_two_levels():
+    # N = 16, p = 4, L = 2: level 0 = tokens (selected), level 1 = 4 blocks (kept whole).
+    # Kept tokens 5 and 9 (causal positions 5, 9); coarsest entries at e = 3, 7, 11, 15.
+    cfg = _cfg(2, 4, 2, 16, mode=O.DIRECT)
+    sizes = O.level_sizes(16, 2, 4)
+    glev, gidx = O.gathered_set({0: np.array([5, 9])}, sizes, cfg)
+    assert list(zip(glev.tolist(), gidx.tolist())) == [
+        (1, 0), (0, 5), (1, 1), (0, 9), (1, 2), (1, 3)]
+    inv = O.inverse_map(glev, gidx, sizes)
+    # scatter of ones: block j of level 1 reaches tokens [4j + 3, 4j + 6]; tokens reach themselves
+    y = O.scatter(np.ones((6, 1)), inv, 16, 4)[:, 0]
+    assert list(y) == [0, 0, 0, 1, 1, 2, 1, 1, 1, 2, 1, 1, 1, 1, 1, 1]
+    dxg = np.arange(6, dtype=np.float64)[:, None] + 1.0
+    dx = O.gather_pool_backward(dxg, inv, 16, 4)[:, 0]
+    assert dx[9] == dxg[3, 0] + dxg[4, 0] / 4   # token 9 itself + block 2 (tokens 8..11)
+    assert dx[5] == dxg[1, 0] + dxg[2, 0] / 4   # token 5 itself + block 1
+    assert dx[0] == dxg[0, 0] / 4
+    assert dx[15] == dxg[5, 0] / 4
+
+
+def test_direct_worked_example_three_levels():
+    # N = 16, p = 2, L = 3: tokens (level 0) and pairs (level 1) are selected, the four
+    # 4-token blocks (level 2) are kept whole.  Kept: token 6 (e = 6); pairs 2 (tokens 4-5,
+    # e = 5) and 5 (tokens 10-11, e = 11).  Pair 5 and block 2 share e = 11: the finer first.
+    cfg = _cfg(3, 2, [1, 2, 0], 16, mode=O.DIRECT)
+    sizes = O.level_sizes(16, 3, 2)
+    glev, gidx = O.gathered_set({0: np.array([6]), 1: np.array([2, 5])}, sizes, cfg)
+    assert list(zip(glev.tolist(), gidx.tolist())) == [
+        (2, 0), (1, 2), (0, 6), (2, 1), (1, 5), (2, 2), (2, 3)]
+    inv = O.inverse_map(glev, gidx, sizes)
+    y = O.scatter(np.ones((7, 1)), inv, 16, 2)[:, 0]
+    # block 0 -> 3..6, pair 2 -> 5..6, token 6 -> 6, block 1 -> 7..10, pair 5 -> 11..12,
+    # block 2 -> 11..14, block 3 -> 15
+    assert list(y) == [0, 0, 0, 1, 1, 2, 3, 1, 1, 1, 1, 2, 2, 1, 1, 1]
+    dxg = np.arange(7, dtype=np.float64)[:, None] + 1.0
+    dx = O.gather_pool_backward(dxg, inv, 16, 2)[:, 0]
+    assert dx[5] == dxg[1, 0] / 2 + dxg[3, 0] / 4
+    assert dx[6] == dxg[2, 0] + dxg[3, 0] / 4
+    assert dx[11] == dxg[4, 0] / 2 + dxg[5, 0] / 4
+    assert dx[0] == dxg[0, 0] / 4
+
+
+def test_direct_full_budget_equals_dense_attention_over_pyramid(rng):
+    # every entry of levels 0..L-2 kept: the gathered set is the whole pyramid
+    n, h, d, L, p = 128, 1, 8, 3, 4
+    x = {w: rng.standard_normal((1, n, h, d)) for w in "qkv"}
+    cfg = _cfg(L, p, 10**6, 16, mode=O.DIRECT)
+    y, _ = O.forward(x["q"], x["k"], x["v"], cfg)
+    ref = _full_pyramid_reference(x["q"][0, :, 0], x["k"][0, :, 0], x["v"][0, :, 0], L, p)
+    assert np.allclose(y[0, :, 0], ref, atol=1e-12)
+
+
+def _library_layer(q, k, v, L, p, chunk, kk, mode, scorer="k"):
+    """One head of the layer rebuilt from library routines (torch avg_pool1d, vector_norm,
+    SDPA) with the brute-force rank count as the selector, without bf16 rounding."""
+    n, d = q.shape
+    t = {a: torch.from_numpy(x).T[None] for a, x in (("q", q), ("k", k), ("v", v))}
+    lv = {a: [F.avg_pool1d(t[a], p**l, p**l)[0].T for l in range(L)] for a in "qkv"}
+    nrm = {a: [torch.linalg.vector_norm(r, dim=1).numpy() for r in lv[a]] for a in "qkv"}
+    if scorer == "k":
+        sc = nrm["k"]
+    elif scorer == "qk":
+        sc = [a * b for a, b in zip(nrm["q"], nrm["k"])]
+    else:
+        sc = [np.sqrt(a**2 + b**2 + c**2) for a, b, c in zip(nrm["q"], nrm["k"], nrm["v"])]
+    levels = range(0, L - 1) if mode == O.DIRECT else range(1, L)
+    ents = [((j + 1) * p ** (L - 1) - 1, L - 1, j) for j in range(n // p ** (L - 1))]
+    for l in levels:
+        for j in _brute_select(sc[l], kk, chunk).tolist():
+            if mode == O.DIRECT:
+                ents.append(((j + 1) * p**l - 1, l, j))
+            else:
+                ents += [((j * p + c + 1) * p ** (l - 1) - 1, l - 1, j * p + c) for c in range(p)]
+    ents.sort()
+    g = {a: torch.stack([lv[a][l][j] for _, l, j in ents]) for a in "qkv"}
+    og = F.scaled_dot_product_attention(g["q"][None], g["k"][None], g["v"][None], is_causal=True)[0]
+    m = torch.zeros(n, len(ents), dtype=torch.float64)
+    for s, (e, l, j) in enumerate(ents):
+        m[e:min(n, e + p**l), s] = 1.0
+    return (m @ og).numpy(), ents
+
+
+@pytest.mark.parametrize("mode", [O.DIRECT, O.REFINE])
+@pytest.mark.parametrize("scorer", ["k", "qk", "qkv"])
+def test_layer_matches_library_reconstruction(rng, mode, scorer):
+    n, d, L, p, kk, chunk = 512, 8, 3, 4, 9, 32
+    x = {w: rng.standard_normal((n, d)) * np.exp(0.5 * rng.standard_normal((n, 1))) for w in "qkv"}
+    cfg = O.Config(L, p, kk, chunk, mode=mode, bf16_attention=False, scorer=scorer)
+    y, st = O.head_forward(x["q"], x["k"], x["v"], cfg)
+    ref, ents = _library_layer(x["q"], x["k"], x["v"], L, p, chunk, kk, mode, scorer)
+    assert list(zip(st.glev.tolist(), st.gidx.tolist())) == [(l, j) for _, l, j in ents]
+    assert np.allclose(y, ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------- scorer variants
+def test_scorer_variants_closed_forms():
+    # one entry per row: q = a e1, k = b e1, v = c e2
+    a = np.array([2.0, -3.0, 0.0, 1.5])
+    b = np.array([4.0, 0.5, 7.0, -2.0])
+    c = np.array([1.0, 6.0, -2.0, 0.0])
+    d = 16
+    qr, kr, vr = (np.zeros((4, d)) for _ in range(3))
+    qr[:, 0], kr[:, 0], vr[:, 1] = a, b, c
+    k_only = O.score_pyramid([kr], "k")[0]
+    qk = O.score_pyramid([kr], "qk", [qr], [vr])[0]
+    qkv = O.score_pyramid([kr], "qkv", [qr], [vr])[0]
+    assert np.array_equal(k_only, np.abs(b))
+    assert np.array_equal(qk, np.abs(a) * np.abs(b))
+    assert np.allclose(qkv, np.sqrt(a**2 + b**2 + c**2), rtol=1e-15)
+    with pytest.raises(ValueError):
+        O.Config(3, 4, 8, 16, scorer="dilated")
+
+
+def test_scorer_variants_change_the_selection():
+    # Two level-1 blocks: block 0 has the larger pooled key, block 1 the larger pooled query
+    # (and value).  The key scorer keeps block 0, the query-key product keeps block 1.
+    n, d, p = 8, 4, 4
+    q, k, v = (np.zeros((n, d)) for _ in range(3))
+    k[0:4, 0] = 3.0
+    k[4:8, 0] = 2.0
+    q[0:4, 1] = 1.0
+    q[4:8, 1] = 5.0
+    v[4:8, 2] = 1.0
+    picks = {}
+    for scorer in ("k", "qk", "qkv"):
+        cfg = O.Config(2, p, 1, 16, bf16_attention=False, scorer=scorer)
+        _, scores, sel = O.head_selection(k, cfg, q=q, v=v)
+        picks[scorer] = sel[1].tolist()
+    assert picks == {"k": [0], "qk": [1], "qkv": [1]}
