@@ -20,7 +20,9 @@ STATUS = {
     0: "LH_OK", -1: "LH_ERR_NULL", -2: "LH_ERR_SHAPE", -3: "LH_ERR_LEVELS", -4: "LH_ERR_POOL",
     -5: "LH_ERR_K", -6: "LH_ERR_CHUNK", -7: "LH_ERR_DTYPE", -8: "LH_ERR_ALIGN",
     -9: "LH_ERR_WORKSPACE", -10: "LH_ERR_LAUNCH", -11: "LH_ERR_UNSUPPORTED",
+    -12: "LH_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 64 << 20
 CODE = {v: k for k, v in STATUS.items()}
 
 
@@ -81,6 +83,7 @@ _SIGS = {
     "lh_scatter_bwd": [_CFG, P, P, P, P, P, P, P],
     "lh_gather_pool_bwd": [_CFG, P, P, P, P, P, P, P, P],
     "lh_forward": [_CFG, P, P, P, P, P, P, ctypes.c_size_t, P],
+    "lh_forward_noalloc": [_CFG, P, P, P, P, P, P],
     "lh_backward": [_CFG, P, P, P, P, P, P, ctypes.c_size_t, P],
 }
 EXPORTS = tuple(_SIGS)

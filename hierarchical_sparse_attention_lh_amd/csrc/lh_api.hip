@@ -5,7 +5,14 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "lh_internal.h"
+
+// Forward workspace of lh_forward_noalloc: one array per GPU, held until the process ends.
+// Host code must never pass this name to a kernel (on the host it is only a stand-in); it
+// uses the device address hipGetSymbolAddress reports for the current device instead.
+static __device__ __align__(256) unsigned char scratch[LH_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -189,6 +196,25 @@ inline const char* at(const void* base, size_t off) {
   return static_cast<const char*>(base) + off;
 }
 
+// Device address of `scratch` on the current device, looked up once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+lh_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LH_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return LH_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LH_OK;
+}
+
 lh_status check_desc(const lh_attn_desc* d) {
   if (d == nullptr) return LH_ERR_NULL;
   if (d->batch < 1 || d->heads < 1 || d->seq < 1 || d->seq > kMaxAttnLen) return LH_ERR_SHAPE;
@@ -215,6 +241,7 @@ const char* lh_status_string(lh_status s) {
     case LH_ERR_WORKSPACE: return "workspace too small";
     case LH_ERR_LAUNCH: return "kernel launch failed";
     case LH_ERR_UNSUPPORTED: return "option not implemented";
+    case LH_ERR_SCRATCH: return "forward workspace exceeds the static scratch of lh_forward_noalloc";
   }
   return "unknown status";
 }
@@ -373,15 +400,14 @@ lh_status lh_gather_pool_bwd(const lh_config* cfg, const int32_t* inv, const flo
                                              dv, st), st);
 }
 
-lh_status lh_forward(const lh_config* cfg, const void* q, const void* k, const void* v,
-                     void* y, void* saved, void* ws, size_t ws_bytes, lh_stream_t stream) {
-  Levels L;
-  LH_TRY(check_config(cfg, &L));
-  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(v)); LH_TRY(need(y)); LH_TRY(need(saved));
-  lh_plan_info P;
-  fill_plan(cfg, L, &P);
-  if (P.ws_forward_bytes > 0) LH_TRY(need(ws));
-  if (ws_bytes < P.ws_forward_bytes) return LH_ERR_WORKSPACE;
+}  // extern "C"
+
+namespace {
+
+// Stages 1-5 on a validated config; `ws` holds at least P.ws_forward_bytes.
+lh_status forward_body(const lh_config* cfg, const Levels& L, const lh_plan_info& P,
+                       const void* q, const void* k, const void* v, void* y, void* saved,
+                       void* ws, lh_stream_t stream) {
   auto st = static_cast<hipStream_t>(stream);
   const int32_t f32 = cfg->dtype == LH_F32;
 
@@ -407,6 +433,35 @@ lh_status lh_forward(const lh_config* cfg, const void* q, const void* k, const v
   LH_TRY(launched(lh::launch_attn_fwd(L.B, L.H, L.S, L.D, P.softmax_scale, rows[0], rows[1],
                                       trans[2], og, lse, st), st));
   return launched(lh::launch_scatter(L, f32, inv, og, y, st), st);
+}
+
+}  // namespace
+
+extern "C" {
+
+lh_status lh_forward(const lh_config* cfg, const void* q, const void* k, const void* v,
+                     void* y, void* saved, void* ws, size_t ws_bytes, lh_stream_t stream) {
+  Levels L;
+  LH_TRY(check_config(cfg, &L));
+  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(v)); LH_TRY(need(y)); LH_TRY(need(saved));
+  lh_plan_info P;
+  fill_plan(cfg, L, &P);
+  if (P.ws_forward_bytes > 0) LH_TRY(need(ws));
+  if (ws_bytes < P.ws_forward_bytes) return LH_ERR_WORKSPACE;
+  return forward_body(cfg, L, P, q, k, v, y, saved, ws, stream);
+}
+
+lh_status lh_forward_noalloc(const lh_config* cfg, const void* q, const void* k, const void* v,
+                             void* y, void* saved, lh_stream_t stream) {
+  Levels L;
+  LH_TRY(check_config(cfg, &L));
+  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(v)); LH_TRY(need(y)); LH_TRY(need(saved));
+  lh_plan_info P;
+  fill_plan(cfg, L, &P);
+  if (P.ws_forward_bytes > LH_NOALLOC_SCRATCH_BYTES) return LH_ERR_SCRATCH;
+  void* ws = nullptr;
+  LH_TRY(scratch_address(&ws));
+  return forward_body(cfg, L, P, q, k, v, y, saved, ws, stream);
 }
 
 lh_status lh_backward(const lh_config* cfg, const void* saved, const void* dy, void* dq,

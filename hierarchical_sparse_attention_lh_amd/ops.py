@@ -238,6 +238,15 @@ def lh_forward(cfg, q, k, v, bufs: Buffers | None = None, y=None):
     return y, bufs
 
 
+def lh_forward_noalloc(cfg, q, k, v, y, saved):
+    """lh_forward with the library's static per-GPU workspace; y and saved are caller-given
+    (saved: a uint8 device tensor of lh_plan(cfg).saved_bytes).  Allocates nothing."""
+    _check_tokens(cfg, q, k, v, y)
+    check(_lib.load().lh_forward_noalloc(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(y),
+                                         _p(saved), _stream()))
+    return y
+
+
 def lh_backward(cfg, bufs: Buffers, dy, dq=None, dk=None, dv=None):
     """Layer backward with the selection lh_forward saved in `bufs`; returns dq, dk, dv."""
     _check_tokens(cfg, dy, dq, dk, dv)

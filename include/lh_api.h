@@ -23,7 +23,8 @@
  * Readings of what the pages leave open (used by every entry point below):
  *   - levels l = 0..L-1, level 0 = raw tokens, n_l = N / p^l; p^(L-1) must divide N.
  *   - score = l2 norm of the pooled KEY row of a head (float32).
- *   - REFINE (the mode implemented): selection runs at levels 1..L-1 with budget
+ *   - REFINE (the default mode; DIRECT below is the literal alternative): selection runs at
+ *     levels 1..L-1 with budget
  *     k_l = min(k[l], n_l); each kept entry enters the gathered sequence as its p children
  *     one level finer, the coarsest level enters whole, so
  *     S = n_{L-1} + p * sum_{l=1}^{L-1} k_l  (about 65K at N = 1e6, L = 4, p = 4, k = 4096).
@@ -41,14 +42,15 @@
  * Conventions for every entry point:
  *   - Pointers marked "device" are caller-owned device memory of the current HIP device;
  *     pointers marked "host" are host memory.  The library keeps no pointer after a call
- *     returns and allocates nothing.
+ *     returns and allocates nothing (lh_forward_noalloc uses a static array instead).
  *   - Every device pointer must be 16-byte aligned (LH_ERR_ALIGN otherwise).
  *   - All arguments are validated on the host before the first launch; a call that
  *     returns an error has launched nothing.  Kernel faults surface at the caller's next
  *     synchronisation (or inside the call when the environment sets LH_DEBUG_SYNC=1).
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = null stream).
  *     No entry point synchronises the host.  Calls on different streams that touch
- *     different buffers may run concurrently; the library has no mutable global state.
+ *     different buffers may run concurrently; the library's only mutable global state is
+ *     the static workspace of lh_forward_noalloc (see there).
  *   - Tensors are dense and row-major.  Token tensors are [B, N, H, D].  Gathered-domain
  *     tensors store Sp = S rounded up to a multiple of 128 slots: rows [B, H, Sp, D],
  *     "transposed" [B, H, D, Sp], per-slot vectors [B, H, Sp].  In a transposed tensor,
@@ -70,6 +72,8 @@ extern "C" {
 #endif
 
 #define LH_MAX_LEVELS 8
+/* size of the static per-GPU workspace of lh_forward_noalloc (64 MiB) */
+#define LH_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef void* lh_stream_t; /* hipStream_t */
 
@@ -87,7 +91,9 @@ typedef enum lh_status {
   LH_ERR_ALIGN = -8,       /* a device pointer is not 16-byte aligned                      */
   LH_ERR_WORKSPACE = -9,   /* workspace smaller than lh_plan reports                       */
   LH_ERR_LAUNCH = -10,     /* the HIP runtime refused a launch                             */
-  LH_ERR_UNSUPPORTED = -11 /* an unknown select_mode                                       */
+  LH_ERR_UNSUPPORTED = -11, /* an unknown select_mode or other option                     */
+  LH_ERR_SCRATCH = -12     /* lh_forward_noalloc: the forward workspace of this config is
+                              larger than LH_NOALLOC_SCRATCH_BYTES                         */
 } lh_status;
 
 typedef enum lh_dtype { LH_BF16 = 0, LH_F32 = 1 } lh_dtype;
@@ -277,6 +283,18 @@ lh_status lh_gather_pool_bwd(const lh_config* cfg, const int32_t* inv, const flo
  *   ws      device workspace of at least ws_forward_bytes (contents undefined after) */
 lh_status lh_forward(const lh_config* cfg, const void* q, const void* k, const void* v,
                      void* y, void* saved, void* ws, size_t ws_bytes, lh_stream_t stream);
+
+/* lh_forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Identical kernels and results; the
+ * forward workspace comes from a static array of LH_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends (looked up once per device with
+ * hipGetSymbolAddress).  Configs with ws_forward_bytes above that size are rejected with
+ * LH_ERR_SCRATCH before anything is launched.  It calls no allocating routine.  Every call on
+ * one GPU shares that GPU's array (whose contents are whatever the last call left; nothing
+ * in it needs to start at zero), so calls that overlap on one GPU -- on different streams or
+ * from different threads -- race: serialise them.  Uses the current HIP device. */
+lh_status lh_forward_noalloc(const lh_config* cfg, const void* q, const void* k, const void* v,
+                             void* y, void* saved, lh_stream_t stream);
 
 /* Backward with the selection frozen at what lh_forward saved.
  *   dy device [B, N, H, D] in cfg->dtype; dq, dk, dv device [B, N, H, D] in cfg->dtype

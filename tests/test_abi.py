@@ -157,3 +157,16 @@ def test_status_strings():
         s = ops.lh_status_string(code)
         assert isinstance(s, str) and s and s != "unknown status"
     assert ops.lh_status_string(12345) == "unknown status"
+
+
+def test_forward_noalloc_rejects_workspace_above_scratch_before_launch():
+    # the 98K layer needs ~0.2 GB of forward workspace: more than the static scratch
+    w = synth.WORKLOADS["layer-98k"]
+    cfg = ops.config_for(w)
+    assert ops.lh_plan(cfg).ws_forward_bytes > _lib.NOALLOC_SCRATCH_BYTES
+    ok = ctypes.c_void_p(0x10000)
+    code = _call("lh_forward_noalloc", ctypes.byref(cfg), ok, ok, ok, ok, ok, None)
+    assert code == _lib.CODE["LH_ERR_SCRATCH"]
+    small = _cfg()
+    assert _call("lh_forward_noalloc", ctypes.byref(small), ok, None, ok, ok, ok, None) == \
+        _lib.CODE["LH_ERR_NULL"]
