@@ -15,6 +15,7 @@ MAX_LEVELS = 8
 
 LH_BF16, LH_F32 = 0, 1
 LH_SEL_REFINE, LH_SEL_DIRECT = 0, 1
+SCORERS = {"k": 0, "qk": 1, "qkv": 2}  # lh_scorer
 
 STATUS = {
     0: "LH_OK", -1: "LH_ERR_NULL", -2: "LH_ERR_SHAPE", -3: "LH_ERR_LEVELS", -4: "LH_ERR_POOL",
@@ -33,7 +34,7 @@ class LhConfig(ctypes.Structure):
         ("levels", ctypes.c_int32), ("pool", ctypes.c_int32),
         ("k", ctypes.c_int32 * MAX_LEVELS), ("chunk", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("select_mode", ctypes.c_int32),
-        ("softmax_scale", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float), ("scorer", ctypes.c_int32),
     ]
 
 

@@ -62,6 +62,8 @@ lh_status check_config(const lh_config* c, Levels* lv) {
   if (c->select_mode != LH_SEL_REFINE && c->select_mode != LH_SEL_DIRECT)
     return LH_ERR_UNSUPPORTED;
   if (c->chunk < 16 || c->chunk > 2048 || (c->chunk & (c->chunk - 1)) != 0) return LH_ERR_CHUNK;
+  if (c->scorer != LH_SCORE_K && c->scorer != LH_SCORE_QK && c->scorer != LH_SCORE_QKV)
+    return LH_ERR_UNSUPPORTED;
 
   Levels L;
   memset(&L, 0, sizeof(L));
@@ -71,6 +73,7 @@ lh_status check_config(const lh_config* c, Levels* lv) {
   L.N = c->n_tokens;
   L.H = c->heads;
   L.D = c->head_dim;
+  L.scorer = c->scorer;
   int64_t pw = 1;
   for (int l = 0; l < L.L; ++l) {
     L.pw[l] = pw;

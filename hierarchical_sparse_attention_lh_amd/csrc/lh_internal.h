@@ -32,6 +32,7 @@ struct Levels {
                                 // enter as their p children), 1 = DIRECT (levels 0..L-2, kept
                                 // entries enter themselves)
   int32_t sel_first, sel_last;  // selected levels (sel_first > sel_last when none)
+  int32_t scorer;               // lh_scorer
 };
 
 // floor(x / p^l) for non-negative x < 2^31, by a shift when p is a power of two.

@@ -4,7 +4,9 @@
 // section "核心方法：金字塔池化与“外部选择”", item 1: Q, K and V are average-pooled together
 // into a multi-level pyramid.  [EN] encorp.ai, "Услуги по внедряване на AI задават правилния
 // въпрос за Lighthouse Attention", section "Как four-stage pipeline остава бърз, без да чупи
-// градиентите?": entries are scored with per-head l2 norms (reading: of the pooled key row).
+// градиентите?": entries are scored with per-head l2 norms (reading: of the pooled key row;
+// [CB] "The Bottom Line" names the same projection-norm scorer, and two further readings are
+// options: ||q_bar|| * ||k_bar|| and the norm of the concatenated [q_bar; k_bar; v_bar]).
 //
 // Design (HBM-bound scan): one thread owns 8 consecutive columns of a token row (one 16-byte
 // bf16 load per token) and walks one coarsest block of p^(L-1) tokens, keeping a float32
@@ -200,9 +202,186 @@ __global__ __launch_bounds__(256) void pool_score_kernel(Levels lv, const Tin* _
   pool_block<L - 1>(c, lv, tile * T, out);
 }
 
+// ------------------------------------------------------------------ scorer variants
+// The "qk" (||q_bar|| * ||k_bar||) and "qkv" (||[q_bar; k_bar; v_bar]||) scorers need the
+// norms of the three pooled rows of one entry together, so here one thread pools Q, K and V
+// of its 8 columns side by side (three loads per token instead of one thread per stream).
+// The per-stream sums of squares are float64, reduced over the head's D/8 lanes before they
+// are combined; the head's first lane writes the float32 score.
+template <typename Tin, typename Tout>
+struct Ctx3 {
+  const Tin* x[3];  // this thread's column in token row 0 of its batch, per stream
+  Tout* px[3];      // this thread's column in pooled row 0 of its batch, per stream (or null)
+  float* sc;        // scores of this (batch, head)
+  int64_t row;
+  int p;
+  float inv_p;
+  int hd8;
+  bool writer;
+  bool score0;
+  int scorer;       // 1 = qk, 2 = qkv
+};
+
+__device__ __forceinline__ double lane_ssq(const float (&v)[8], int hd8) {
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss += static_cast<double>(v[i]) * static_cast<double>(v[i]);
+  for (int m = 1; m < hd8; m <<= 1) ss += __shfl_xor(ss, m);
+  return ss;
+}
+
+template <typename Tin, typename Tout>
+__device__ __forceinline__ void score3(const Ctx3<Tin, Tout>& c, const Levels& lv, int level,
+                                       int64_t j, const float (&vq)[8], const float (&vk)[8],
+                                       const float (&vv)[8]) {
+  const double sq = lane_ssq(vq, c.hd8);
+  const double sk = lane_ssq(vk, c.hd8);
+  double s;
+  if (c.scorer == 1) {
+    s = sqrt(sq) * sqrt(sk);
+  } else {
+    const double sv = lane_ssq(vv, c.hd8);
+    s = sqrt(sq + sk + sv);
+  }
+  if (c.writer) c.sc[lv.off[level] + j] = static_cast<float>(s);
+}
+
+template <typename Tin, typename Tout>
+__device__ __forceinline__ void emit3(const Ctx3<Tin, Tout>& c, const Levels& lv, int level,
+                                      int64_t j, const float (&v)[3][8]) {
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+    if (c.px[s]) store8(c.px[s] + (lv.poff[level] + j) * c.row, v[s]);
+  score3(c, lv, level, j, v[0], v[1], v[2]);
+}
+
+// Mean of the p tokens from t0 for all three streams; four tokens' loads are in flight at a
+// time per stream.
+template <typename Tin, typename Tout>
+__device__ __forceinline__ void level1_3(const Ctx3<Tin, Tout>& c, const Levels& lv, int64_t t0,
+                                         float (&out)[3][8]) {
+  float acc[3][8];
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[s][e] = 0.f;
+  for (int i0 = 0; i0 < c.p; i0 += 4) {
+    float v[3][4][8];
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u < c.p) load8(c.x[s] + (t0 + i0 + u) * c.row, v[s][u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u < c.p) {
+        if (c.score0) score3(c, lv, 0, t0 + i0 + u, v[0][u], v[1][u], v[2][u]);
+#pragma unroll
+        for (int s = 0; s < 3; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[s][e] += v[s][u][e];
+      }
+  }
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[s][e] = acc[s][e] * c.inv_p;
+}
+
+template <int LVL, typename Tin, typename Tout>
+__device__ __forceinline__ void pool_block3(const Ctx3<Tin, Tout>& c, const Levels& lv,
+                                            int64_t t0, float (&out)[3][8]) {
+  if constexpr (LVL == 1) {
+    level1_3(c, lv, t0, out);
+  } else {
+    float acc[3][8];
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[s][e] = 0.f;
+    const int64_t span = lv.pw[LVL - 1];
+    for (int i = 0; i < c.p; ++i) {
+      float ch[3][8];
+      pool_block3<LVL - 1>(c, lv, t0 + i * span, ch);
+#pragma unroll
+      for (int s = 0; s < 3; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[s][e] += ch[s][e];
+    }
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[s][e] = acc[s][e] * c.inv_p;
+  }
+  emit3(c, lv, LVL, t0 / lv.pw[LVL], out);
+}
+
+template <int L, typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void pool_score3_kernel(Levels lv, int scorer,
+                                                          const Tin* __restrict__ q,
+                                                          const Tin* __restrict__ k,
+                                                          const Tin* __restrict__ v,
+                                                          Tout* pq, Tout* pk, Tout* pv,
+                                                          float* scores) {
+  const int64_t G = static_cast<int64_t>(lv.H) * lv.D / 8;
+  const int64_t T = lv.pw[L - 1];
+  const int64_t tiles = lv.N / T;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= lv.B * tiles * G) return;
+  const int64_t g = gid % G;
+  const int64_t tt = gid / G;
+  const int64_t tile = tt % tiles;
+  const int64_t b = tt / tiles;
+  const int hd8 = lv.D / 8;
+  const int64_t h = g / hd8;
+
+  Ctx3<Tin, Tout> c;
+  c.row = G * 8;
+  const Tin* xs[3] = {q, k, v};
+  Tout* ps[3] = {pq, pk, pv};
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    c.x[s] = xs[s] + b * lv.N * c.row + g * 8;
+    c.px[s] = ps[s] ? ps[s] + b * lv.P1 * c.row + g * 8 : nullptr;
+  }
+  c.sc = scores + (b * lv.H + h) * lv.P;
+  c.p = lv.p;
+  c.inv_p = 1.0f / static_cast<float>(lv.p);
+  c.hd8 = hd8;
+  c.writer = (g % hd8) == 0;
+  c.score0 = lv.direct;
+  c.scorer = scorer;
+
+  float out[3][8];
+  pool_block3<L - 1>(c, lv, tile * T, out);
+}
+
 template <typename Tin, typename Tout>
 hipError_t dispatch(const Levels& lv, const void* q, const void* k, const void* v, void* pq,
                     void* pk, void* pv, float* scores, hipStream_t st) {
+  if (lv.scorer != LH_SCORE_K) {
+    const int64_t G = static_cast<int64_t>(lv.H) * lv.D / 8;
+    const int64_t total = lv.B * (lv.N / lv.pw[lv.L - 1]) * G;
+    dim3 grid(static_cast<unsigned>((total + 255) / 256));
+    const int sc = lv.scorer == LH_SCORE_QK ? 1 : 2;
+    auto args3 = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, lv, sc, static_cast<const Tin*>(q),
+                         static_cast<const Tin*>(k), static_cast<const Tin*>(v),
+                         static_cast<Tout*>(pq), static_cast<Tout*>(pk), static_cast<Tout*>(pv),
+                         scores);
+    };
+    switch (lv.L) {
+      case 2: args3(pool_score3_kernel<2, Tin, Tout>); break;
+      case 3: args3(pool_score3_kernel<3, Tin, Tout>); break;
+      case 4: args3(pool_score3_kernel<4, Tin, Tout>); break;
+      case 5: args3(pool_score3_kernel<5, Tin, Tout>); break;
+      case 6: args3(pool_score3_kernel<6, Tin, Tout>); break;
+      case 7: args3(pool_score3_kernel<7, Tin, Tout>); break;
+      case 8: args3(pool_score3_kernel<8, Tin, Tout>); break;
+      default: return hipSuccess;
+    }
+    return hipGetLastError();
+  }
   const int64_t G = static_cast<int64_t>(lv.H) * lv.D / 8;
   const int64_t total = lv.B * (lv.N / lv.pw[lv.L - 1]) * G;
   dim3 grid(static_cast<unsigned>((total + 255) / 256), 3);

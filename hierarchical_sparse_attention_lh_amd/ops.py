@@ -18,8 +18,9 @@ _TORCH_DTYPE = {LH_BF16: torch.bfloat16, LH_F32: torch.float32}
 
 
 def make_config(batch, n_tokens, heads, head_dim, levels, pool, k, chunk, dtype="bf16",
-                scale=0.0, select_mode=LH_SEL_REFINE) -> LhConfig:
-    """Fill an lh_config.  `k` is one budget for every level or a per-level list."""
+                scale=0.0, select_mode=LH_SEL_REFINE, scorer="k") -> LhConfig:
+    """Fill an lh_config.  `k` is one budget for every level or a per-level list; `scorer`
+    is "k", "qk" or "qkv" (or the lh_scorer code)."""
     cfg = LhConfig()
     cfg.batch, cfg.n_tokens, cfg.heads, cfg.head_dim = batch, n_tokens, heads, head_dim
     cfg.levels, cfg.pool, cfg.chunk = levels, pool, chunk
@@ -29,13 +30,15 @@ def make_config(batch, n_tokens, heads, head_dim, levels, pool, k, chunk, dtype=
     cfg.dtype = {"bf16": LH_BF16, "f32": LH_F32}.get(dtype, dtype)
     cfg.select_mode = select_mode
     cfg.softmax_scale = scale
+    cfg.scorer = _lib.SCORERS.get(scorer, scorer)
     return cfg
 
 
 def config_for(w) -> LhConfig:
     """lh_config of a synth.Workload."""
     return make_config(w.batch, w.n_tokens, w.heads, w.head_dim, w.levels, w.pool, w.k, w.chunk,
-                       w.dtype, select_mode=LH_SEL_DIRECT if w.mode == "direct" else LH_SEL_REFINE)
+                       w.dtype, select_mode=LH_SEL_DIRECT if w.mode == "direct" else LH_SEL_REFINE,
+                       scorer=w.scorer)
 
 
 def torch_dtype(cfg: LhConfig):

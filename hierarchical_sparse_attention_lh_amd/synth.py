@@ -43,6 +43,7 @@ class Workload:
     seed: int
     backward: bool
     mode: str = "refine"  # selection reading: "refine" (the contract) or "direct"
+    scorer: str = "k"  # score of a pooled entry: "k", "qk" or "qkv"
 
 
 WORKLOADS = {

@@ -22,7 +22,8 @@
  *
  * Readings of what the pages leave open (used by every entry point below):
  *   - levels l = 0..L-1, level 0 = raw tokens, n_l = N / p^l; p^(L-1) must divide N.
- *   - score = l2 norm of the pooled KEY row of a head (float32).
+ *   - score = l2 norm of the pooled KEY row of a head (float32); lh_scorer offers two
+ *     further readings.
  *   - REFINE (the default mode; DIRECT below is the literal alternative): selection runs at
  *     levels 1..L-1 with budget
  *     k_l = min(k[l], n_l); each kept entry enters the gathered sequence as its p children
@@ -105,6 +106,14 @@ typedef enum lh_dtype { LH_BF16 = 0, LH_F32 = 1 } lh_dtype;
  * (S = n_{L-1} + sum k_l).  In both the coarsest level enters whole. */
 typedef enum lh_select_mode { LH_SEL_REFINE = 0, LH_SEL_DIRECT = 1 } lh_select_mode;
 
+/* What an entry's score is (the pages name a parameter-free per-head l2-norm scorer -- the
+ * projection-norm scorer of [CB] "The Bottom Line" -- without naming the vector):
+ * K   = ||k_bar||, the pooled key row's norm (the default reading);
+ * QK  = ||q_bar|| * ||k_bar||;
+ * QKV = ||[q_bar; k_bar; v_bar]|| = sqrt(||q_bar||^2 + ||k_bar||^2 + ||v_bar||^2).
+ * Norms are per head, of the float32 pooled rows, summed in float64. */
+typedef enum lh_scorer { LH_SCORE_K = 0, LH_SCORE_QK = 1, LH_SCORE_QKV = 2 } lh_scorer;
+
 /* Problem statement of one layer call: the pages' N, heads, head_dim, L, p, per-level k and
    chunk size ([EN] attention-path section gives N, L, p, k; [WS] item 2 the chunked top-K). */
 typedef struct lh_config {
@@ -121,6 +130,7 @@ typedef struct lh_config {
   int32_t dtype;          /* lh_dtype of Q, K, V, Y, dY, dQ, dK, dV                       */
   int32_t select_mode;    /* lh_select_mode                                               */
   float softmax_scale;    /* <= 0 selects 1/sqrt(D)                                       */
+  int32_t scorer;         /* lh_scorer (0 = K, the l2 norm of the pooled key row)          */
 } lh_config;
 
 /* Sizes derived from a config by closed forms (host struct filled by lh_plan). */
@@ -165,8 +175,8 @@ const char* lh_status_string(lh_status status);
  *   scores   device float32 [B, H, pyramid_total], indexed by pyramid id; levels 1..L-1 are
  *            written, and level 0 (the raw key rows) too in DIRECT; REFINE leaves level 0
  *            untouched
- *   Any of pq/pk/pv may be NULL to skip that stream's pooled output (scores still come
- *   from K).  With L = 1 nothing is launched. */
+ *   Any of pq/pk/pv may be NULL to skip that stream's pooled output (scores are computed
+ *   either way).  With L = 1 nothing is launched. */
 lh_status lh_pool_score(const lh_config* cfg, const void* q, const void* k, const void* v,
                         void* pq, void* pk, void* pv, int32_t pooled_dtype, float* scores,
                         lh_stream_t stream);

@@ -43,7 +43,8 @@ def inputs(w, with_grad=True):
 
 
 def ocfg(w):
-    return O.Config(w.levels, w.pool, w.k, w.chunk, mode=O.DIRECT if w.mode == "direct" else O.REFINE)
+    return O.Config(w.levels, w.pool, w.k, w.chunk, mode=O.DIRECT if w.mode == "direct" else O.REFINE,
+                    scorer=w.scorer)
 
 
 def sel_levels(w):
@@ -79,8 +80,17 @@ DIRECT_P2 = synth.Workload("direct-p2-d128", 1, 2048, 2, 128, "bf16", 4, 2, 64, 
 # whole pyramid is gathered, S = 1024 + 256 + 64; level 2 is a single chunk of exactly C)
 EMPTY_SEL = synth.Workload("empty-sel", 1, 2048, 2, 64, "bf16", 3, 4, 0, 64, 18, True)
 FULL_BUDGET = synth.Workload("full-budget", 1, 1024, 2, 64, "bf16", 3, 4, 1000, 64, 19, True)
-STAGE_CASES = [TINY, RAGGED, WIDE, POOL2, POOL3, DIRECT, DIRECT_P2, EMPTY_SEL, FULL_BUDGET]
-E2E_CASES = [TINY, RAGGED, WIDE, DENSE, POOL2, POOL3, DIRECT, DIRECT_P2, EMPTY_SEL, FULL_BUDGET]
+# the scorer readings: ||q_bar|| * ||k_bar|| and ||[q_bar; k_bar; v_bar]|| (also under DIRECT,
+# where raw tokens are scored too, at D = 128 and p = 2, and with float32 inputs)
+SCORER_QK = synth.Workload("scorer-qk", 1, 4096, 2, 64, "bf16", 3, 4, 100, 64, 20, True,
+                           scorer="qk")
+SCORER_QKV_DIRECT = synth.Workload("scorer-qkv-direct-d128", 1, 2048, 2, 128, "bf16", 4, 2, 64,
+                                   128, 21, True, "direct", scorer="qkv")
+SCORER_QKV_F32 = synth.Workload("scorer-qkv-f32", 1, 4096, 2, 64, "f32", 3, 4, 128, 64, 22, True,
+                                scorer="qkv")
+SCORER_CASES = [SCORER_QK, SCORER_QKV_DIRECT, SCORER_QKV_F32]
+STAGE_CASES = [TINY, RAGGED, WIDE, POOL2, POOL3, DIRECT, DIRECT_P2, EMPTY_SEL, FULL_BUDGET] + SCORER_CASES
+E2E_CASES = [TINY, RAGGED, WIDE, DENSE, POOL2, POOL3, DIRECT, DIRECT_P2, EMPTY_SEL, FULL_BUDGET] + SCORER_CASES
 
 
 def pooled_rows_oracle(x, w):
@@ -99,31 +109,27 @@ def test_pool_score(w):
     pq, pk, pv, sc = ops.lh_pool_score(cfg, t["q"], t["k"], t["v"], pooled_dtype=torch.float32)
     torch.cuda.synchronize()
     worst_rel = 0.0
+    ref = {name: pooled_rows_oracle(x[name], w) for name in "qkv"}
     for name, p in (("q", pq), ("k", pk), ("v", pv)):
         got = f64(p)
-        ref = pooled_rows_oracle(x[name], w)
         for b in range(w.batch):
             for h in range(w.heads):
                 for lv in range(1, w.levels):
                     o = info.pooled_offset[lv]
                     g = got[b, o:o + info.level_size[lv], h]
-                    r = ref[b][h][lv]
+                    r = ref[name][b][h][lv]
                     scale = np.maximum(np.abs(r), np.linalg.norm(r, axis=1, keepdims=True) / np.sqrt(w.head_dim))
                     assert np.all(np.abs(g - r) <= 1e-4 * scale + 1e-30), (name, b, h, lv)
-                    if name == "k":
-                        s_ref = O.score_pyramid([r])[0]
-                        s_got = f64(sc[b, h, info.level_offset[lv]:info.level_offset[lv] + info.level_size[lv]])
-                        rel = np.abs(s_got - s_ref) / np.maximum(s_ref, 1e-30)
-                        worst_rel = max(worst_rel, float(rel.max()))
-                        assert np.all(rel <= 1e-4), (b, h, lv)
-    if w.mode == "direct":  # the raw key rows are scored too
-        for b in range(w.batch):
-            for h in range(w.heads):
-                s_ref = np.linalg.norm(x["k"][b, :, h].astype(np.float64), axis=1)
-                s_got = f64(sc[b, h, :w.n_tokens])
-                rel = np.abs(s_got - s_ref) / np.maximum(s_ref, 1e-30)
+    # scores of the scored levels (the raw tokens too under DIRECT) against the oracle's scorer
+    first = 0 if w.mode == "direct" else 1
+    for b in range(w.batch):
+        for h in range(w.heads):
+            s_ref = O.score_pyramid(ref["k"][b][h], w.scorer, ref["q"][b][h], ref["v"][b][h])
+            for lv in range(first, w.levels):
+                s_got = f64(sc[b, h, info.level_offset[lv]:info.level_offset[lv] + info.level_size[lv]])
+                rel = np.abs(s_got - s_ref[lv]) / np.maximum(s_ref[lv], 1e-30)
                 worst_rel = max(worst_rel, float(rel.max()))
-                assert np.all(rel <= 1e-4), (b, h, 0)
+                assert np.all(rel <= 1e-4), (b, h, lv)
     print(f"[{w.name}] worst score relative error {worst_rel:.3e}")
     # bf16 pooled output is the same float32 value rounded once
     pq16, pk16, pv16, sc16 = ops.lh_pool_score(cfg, t["q"], t["k"], t["v"], pooled_dtype=torch.bfloat16)
@@ -157,7 +163,7 @@ def test_topk_exact_on_gpu_scores(w):
                 assert np.array_equal(got, want[lv]), (b, h, lv)
 
 
-@pytest.mark.parametrize("w", [TINY, MEDIUM], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [TINY, MEDIUM, SCORER_QK, SCORER_QKV_DIRECT], ids=lambda w: w.name)
 def test_topk_against_float64_scores_with_near_ties(w):
     t, x = inputs(w, with_grad=False)
     cfg = ops.config_for(w)
@@ -167,7 +173,9 @@ def test_topk_against_float64_scores_with_near_ties(w):
     swaps = 0
     for b in range(w.batch):
         for h in range(w.heads):
-            _, scores, want = O.head_selection(x["k"][b, :, h].astype(np.float64), ocfg(w))
+            _, scores, want = O.head_selection(x["k"][b, :, h].astype(np.float64), ocfg(w),
+                                               q=x["q"][b, :, h].astype(np.float64),
+                                               v=x["v"][b, :, h].astype(np.float64))
             for lv in sel_levels(w):
                 o = info.sel_offset[lv]
                 got = set(sel[b, h, o:o + info.k_eff[lv]].tolist())
