@@ -26,6 +26,32 @@ def f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def check_selection(got_sel, own, scores, levels, info, w):
+    """The GPU's kept indices per level against the oracle's float64 selection: ascending,
+    per-chunk counts equal to the quotas, and inside every chunk any difference is a swap
+    of two entries whose float64 scores are within 1e-6 relative (a near tie).  Returns the
+    GPU selection as {level: indices} and the number of forgiven swaps."""
+    gsel, swaps = {}, 0
+    for lv in levels:
+        o = info.sel_offset[lv]
+        got = got_sel[o:o + info.k_eff[lv]].astype(np.int64)
+        assert np.all(np.diff(got) > 0), lv
+        nch, width = O.chunk_layout(info.level_size[lv], w.chunk)
+        quotas = O.chunk_quotas(int(info.k_eff[lv]), nch)
+        assert np.bincount(got // width, minlength=nch).tolist() == quotas, lv
+        s = scores[lv]
+        for c in range(nch):
+            g_c = got[(got >= c * width) & (got < (c + 1) * width)]
+            o_c = own[lv][(own[lv] >= c * width) & (own[lv] < (c + 1) * width)]
+            extra, missing = np.setdiff1d(g_c, o_c), np.setdiff1d(o_c, g_c)
+            assert len(extra) == len(missing), (lv, c)
+            for a, m in zip(extra, missing):
+                assert abs(s[a] - s[m]) <= 1e-6 * max(s[a], s[m]), (lv, c, a, m)
+                swaps += 1
+        gsel[lv] = got
+    return gsel, swaps
+
+
 def workload(name):
     if name.endswith("-direct"):  # the same inputs under the DIRECT selection reading
         return dataclasses.replace(synth.WORKLOADS[name[:-len("-direct")]], name=name,
@@ -60,20 +86,7 @@ def test_full_size_heads_against_oracle(name, heads):
     for h in heads:
         q, k, v, dy = (x[n][0, :, h].astype(np.float64) for n in ("q", "k", "v", "dy"))
         _, scores, own = O.head_selection(k, ocfg)
-        gsel = {}
-        swaps = 0
-        for lv in levels:
-            o = info.sel_offset[lv]
-            got = sel_np[0, h, o:o + info.k_eff[lv]].astype(np.int64)
-            assert np.all(np.diff(got) > 0)
-            gsel[lv] = got
-            extra = np.setdiff1d(got, own[lv])
-            missing = np.setdiff1d(own[lv], got)
-            assert len(extra) == len(missing)
-            s = scores[lv]
-            for a, m in zip(extra, missing):  # only near ties may differ
-                assert abs(s[a] - s[m]) <= 1e-6 * max(s[a], s[m]), (h, lv, a, m)
-                swaps += 1
+        gsel, swaps = check_selection(sel_np[0, h], own, scores, levels, info, w)
         ry, st = O.head_forward(q, k, v, ocfg, sel=gsel)
         assert np.array_equal(gmap_np[0, h, :info.gathered_len], offs[st.glev] + st.gidx)
         rq, rk, rv = O.head_backward(dy, st, ocfg)
@@ -86,3 +99,38 @@ def test_full_size_heads_against_oracle(name, heads):
             assert np.all(err <= tol), (name, h, nm, float(err.max()))
         print(f"[{name} head {h}] near-tie swaps {swaps}; worst err/tol "
               + ", ".join(f"{k_}={v_:.3f}" for k_, v_ in worst.items()))
+
+
+@pytest.mark.parametrize("name", ["lh-512k", "stress-1m", "lh-512k-direct"])
+def test_full_size_selection_and_map_every_head(name):
+    """Every head of the full-size workloads: selection (per-chunk quotas, near-tie rule
+    against the oracle's float64 scores) and the gathered map and its inverse bit-exact for
+    the GPU's selection, through the stage entry points bench.py times."""
+    w = workload(name)
+    x = synth.workload_inputs(w, with_grad=False)
+    t = {n: torch.from_numpy(a).to("cuda").to(torch.bfloat16) for n, a in x.items()}
+    cfg = ops.config_for(w)
+    info = ops.lh_plan(cfg)
+    _, _, _, sc = ops.lh_pool_score(cfg, t["q"], t["k"], t["v"], pooled_dtype=torch.bfloat16)
+    sel = ops.lh_topk(cfg, sc)
+    gmap, inv = ops.lh_build_map(cfg, sel)
+    torch.cuda.synchronize()
+    sel_np, gmap_np, inv_np = sel.cpu().numpy(), gmap.cpu().numpy(), inv.cpu().numpy()
+    direct = w.mode == "direct"
+    ocfg = O.Config(w.levels, w.pool, w.k, w.chunk, mode=O.DIRECT if direct else O.REFINE)
+    levels = range(0, w.levels - 1) if direct else range(1, w.levels)
+    sizes = [info.level_size[l] for l in range(w.levels)]
+    offs = np.array([info.level_offset[l] for l in range(w.levels)])
+    S = info.gathered_len
+    total = 0
+    for h in range(w.heads):
+        _, scores, own = O.head_selection(x["k"][0, :, h].astype(np.float64), ocfg)
+        gsel, swaps = check_selection(sel_np[0, h], own, scores, levels, info, w)
+        total += swaps
+        glev, gidx = O.gathered_set(gsel, sizes, ocfg)
+        ids = offs[glev] + gidx
+        assert np.array_equal(gmap_np[0, h, :S], ids), h
+        want_inv = np.full(info.pyramid_total, -1)
+        want_inv[ids] = np.arange(S)
+        assert np.array_equal(inv_np[0, h], want_inv), h
+    print(f"[{name}] all {w.heads} heads: selection and map exact; forgiven near-tie swaps {total}")
