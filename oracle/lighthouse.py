@@ -281,28 +281,31 @@ def inverse_map(glev: np.ndarray, gidx: np.ndarray, sizes: list) -> list:
 # --------------------------------------------------------------------------------------
 # stage 4b: causal attention on the gathered sequence   ([WS] item 3; [HE] "How ...")
 # --------------------------------------------------------------------------------------
-def causal_attention(q, k, v, scale, rows=512):
+def causal_attention(q, k, v, scale, rows=512, causal=True):
     """O[s] = sum_{s' <= s} softmax_{s'}(scale * q[s].k[s']) v[s'], with the log-sum-exp.
 
-    Plain softmax attention (reading R8): no dropout, bias, window or sink.
+    Plain softmax attention (reading R8): no dropout, bias, window or sink.  With
+    causal=False every key is attended (the same softmax without the mask).
     """
     n = q.shape[0]
     o = np.zeros((n, v.shape[1]))
     lse = np.zeros(n)
     for r0 in range(0, n, rows):
         r1 = min(n, r0 + rows)
-        logits = (q[r0:r1] @ k[:r1].T) * scale
-        future = np.arange(r1)[None, :] > np.arange(r0, r1)[:, None]
-        logits[future] = -np.inf
+        kend = r1 if causal else k.shape[0]
+        logits = (q[r0:r1] @ k[:kend].T) * scale
+        future = np.arange(kend)[None, :] > np.arange(r0, r1)[:, None]
+        if causal:
+            logits[future] = -np.inf
         m = logits.max(axis=1, keepdims=True)
         w = np.exp(logits - m)
         z = w.sum(axis=1, keepdims=True)
-        o[r0:r1] = (w / z) @ v[:r1]
+        o[r0:r1] = (w / z) @ v[:kend]
         lse[r0:r1] = (m + np.log(z))[:, 0]
     return o, lse
 
 
-def causal_attention_backward(q, k, v, o, lse, do, scale, rows=512):
+def causal_attention_backward(q, k, v, o, lse, do, scale, rows=512, causal=True):
     """Gradients of causal_attention for upstream gradient do (selection frozen).
 
     With P the attention weights: dV = P^T dO; dP = dO V^T; dS = P * (dP - rowsum(dO*O));
@@ -315,15 +318,17 @@ def causal_attention_backward(q, k, v, o, lse, do, scale, rows=512):
     delta = np.sum(do * o, axis=1)
     for r0 in range(0, n, rows):
         r1 = min(n, r0 + rows)
-        logits = (q[r0:r1] @ k[:r1].T) * scale
-        future = np.arange(r1)[None, :] > np.arange(r0, r1)[:, None]
-        logits[future] = -np.inf
+        kend = r1 if causal else k.shape[0]
+        logits = (q[r0:r1] @ k[:kend].T) * scale
+        future = np.arange(kend)[None, :] > np.arange(r0, r1)[:, None]
+        if causal:
+            logits[future] = -np.inf
         p = np.exp(logits - lse[r0:r1, None])
-        dv[:r1] += p.T @ do[r0:r1]
-        dp = do[r0:r1] @ v[:r1].T
+        dv[:kend] += p.T @ do[r0:r1]
+        dp = do[r0:r1] @ v[:kend].T
         ds = p * (dp - delta[r0:r1, None])
-        dq[r0:r1] = scale * (ds @ k[:r1])
-        dk[:r1] += scale * (ds.T @ q[r0:r1])
+        dq[r0:r1] = scale * (ds @ k[:kend])
+        dk[:kend] += scale * (ds.T @ q[r0:r1])
     return dq, dk, dv
 
 

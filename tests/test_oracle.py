@@ -283,6 +283,34 @@ def test_attention_matches_torch_sdpa(rng):
     assert np.allclose(lse, torch.logsumexp(logits, 1).numpy(), atol=1e-12)
 
 
+def test_full_attention_matches_torch_sdpa_and_autograd(rng):
+    # causal=False: the same softmax attention over every key
+    s, d = 200, 8
+    q, k, v, do = (rng.standard_normal((s, d)) for _ in range(4))
+    o, lse = O.causal_attention(q, k, v, 0.4, rows=64, causal=False)
+    ts = {a: torch.tensor(x, requires_grad=True) for a, x in (("q", q), ("k", k), ("v", v))}
+    ref = F.scaled_dot_product_attention(ts["q"][None], ts["k"][None], ts["v"][None], scale=0.4)[0]
+    assert np.allclose(o, ref.detach().numpy(), atol=1e-12)
+    assert np.allclose(lse, torch.logsumexp(torch.from_numpy(q @ k.T * 0.4), 1).numpy(), atol=1e-12)
+    ref.backward(torch.from_numpy(do))
+    grads = O.causal_attention_backward(q, k, v, o, lse, do, 0.4, rows=64, causal=False)
+    for a, g in zip("qkv", grads):
+        assert np.allclose(g, ts[a].grad.numpy(), atol=1e-11), a
+
+
+def test_causal_attention_backward_matches_torch_autograd(rng):
+    s, d = 150, 8
+    q, k, v, do = (rng.standard_normal((s, d)) for _ in range(4))
+    o, lse = O.causal_attention(q, k, v, 0.3, rows=32)
+    ts = {a: torch.tensor(x, requires_grad=True) for a, x in (("q", q), ("k", k), ("v", v))}
+    ref = F.scaled_dot_product_attention(ts["q"][None], ts["k"][None], ts["v"][None],
+                                         is_causal=True, scale=0.3)[0]
+    ref.backward(torch.from_numpy(do))
+    grads = O.causal_attention_backward(q, k, v, o, lse, do, 0.3, rows=32)
+    for a, g in zip("qkv", grads):
+        assert np.allclose(g, ts[a].grad.numpy(), atol=1e-11), a
+
+
 def test_single_level_is_textbook_causal_sdpa(rng):
     n, h, d = 256, 2, 16
     x = {w: rng.standard_normal((1, n, h, d)) for w in "qkv"}
