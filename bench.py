@@ -2,11 +2,12 @@
 """Lighthouse attention layer benchmark on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input: pool+score,
-chunked top-K, map, gather, causal attention, scatter (forward), then scatter backward, the
-two attention backward passes and gather+pool backward.  The steps run through the library's
-stage entry points (the same kernels lh_forward / lh_backward launch, in the same order) with
-HIP events recorded between stages on the launch stream, so every kernel's time comes from
-the timed steps themselves.  Inputs are resident in HBM before timing starts.
+chunked top-K, map, causal attention reading its rows through the map, scatter (forward),
+then scatter backward, the two attention backward passes and gather+pool backward.  The
+steps run through the library's stage entry points (the same kernels lh_forward /
+lh_backward launch, in the same order) with HIP events recorded between stages on the launch
+stream, so every kernel's time comes from the timed steps themselves.  Inputs are resident
+in HBM before timing starts.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -18,13 +19,23 @@ import dataclasses
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = "Lighthouse fwd+bwd tokens/sec/layer at 512K on 1 GPU; % HBM and MFMA peak"
+METRIC = "Lighthouse fwd+bwd tokens/sec/layer at {n} on 1 GPU; % HBM and MFMA peak"
+
+
+def metric_name(n_tokens):
+    """The metric string, labelled with the token count actually run (512K for 524,288)."""
+    if n_tokens % 1024 == 0:
+        label = f"{n_tokens // 1024}K" if n_tokens < 1 << 20 else f"{n_tokens / 2**20:g}M"
+    else:
+        label = f"{n_tokens} tokens"
+    return METRIC.format(n=label)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
@@ -37,12 +48,12 @@ def algorithmic(w, info):
     """Per-launch algorithmic work of each stage (bytes for HBM stages, flops for attention).
 
     Each stage counts its own inputs read once and outputs written once, at the dtypes the
-    path stores: pooled levels bf16, scores float32, indices int32, gathered rows bf16,
-    Og / LSE / gathered gradients float32.
+    path stores: pooled levels bf16, scores float32, indices int32, Og / LSE / gathered
+    gradients float32, dOg bf16; index maps count one read per pyramid entry (inv) or slot
+    (gmap).  The attention reads its rows through gmap, so no gather stage exists.
     """
     B, N, H, D = w.batch, w.n_tokens, w.heads, w.head_dim
-    S, Sp, P, P1, K = (info.gathered_len, info.gathered_pad, info.pyramid_total,
-                       info.pooled_rows, info.sel_total)
+    S, P, P1, K = info.gathered_len, info.pyramid_total, info.pooled_rows, info.sel_total
     e = 2 if w.dtype == "bf16" else 4  # token-tensor element size
     BH = B * H
     pairs = BH * S * (S + 1) / 2
@@ -54,12 +65,11 @@ def algorithmic(w, info):
     by = {
         "pool_score": 3 * B * N * H * D * e + 3 * B * P1 * H * D * 2 + BH * scored * 4,
         "topk": BH * selected * 4 + BH * K * 4,
-        "build_map": BH * K * 4 + BH * P * 4 + BH * S * 8,
-        "gather": BH * S * 4 + 3 * BH * S * D * 2 + 6 * BH * S * D * 2,
-        "scatter": BH * S * D * 4 + B * N * H * D * e + BH * N * w.levels * 4,
-        "scatter_bwd": B * N * H * D * e + BH * S * 4 + BH * S * D * 4 + 2 * BH * S * D * 2
+        "build_map": BH * K * 4 + BH * P * 4 + BH * S * 4,
+        "scatter": BH * S * D * 4 + BH * P * 4 + B * N * H * D * e,
+        "scatter_bwd": B * N * H * D * e + BH * S * 4 + BH * S * D * 4 + BH * S * D * 2
                        + BH * S * 4,
-        "gather_pool_bwd": 3 * BH * S * D * 4 + 3 * B * N * H * D * e + BH * N * w.levels * 4,
+        "gather_pool_bwd": 3 * BH * S * D * 4 + BH * P * 4 + 3 * B * N * H * D * e,
     }
     fl = {
         "attn_fwd": 2 * 2 * D * pairs,        # Q K^T and P V
@@ -69,8 +79,8 @@ def algorithmic(w, info):
     return by, fl
 
 
-KERNEL_OF_STAGE = {"attn_fwd": "attn_fwd_d{d}", "attn_bwd_dkdv": "attn_bwd_kv_d{d}",
-                   "attn_bwd_dq": "attn_bwd_q_d{d}"}
+KERNEL_OF_STAGE = {"attn_fwd": "attn_fwd_mapped_d{d}", "attn_bwd_dkdv": "attn_bwd_kv_mapped_d{d}",
+                   "attn_bwd_dq": "attn_bwd_q_mapped_d{d}"}
 
 
 def measured_traffic(workload, stage, head_dim):
@@ -110,11 +120,9 @@ def time_staged(layer, steps, warmup, torch):
         layer.run(stages, between=lambda i, n, s=s: ev[s][i + 1].record())
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {n: 0.0 for n in names}
-    for s in range(steps):
-        for i, n in enumerate(names):
-            per[n] += ev[s][i].elapsed_time(ev[s][i + 1])
-    per = {n: v / steps for n, v in per.items()}
+    # per-stage medians over the timed steps; the step time is the mean
+    per = {n: statistics.median(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps))
+           for i, n in enumerate(names)}
     gpu_step = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)) / steps
     return wall / steps * 1e3, gpu_step, per
 
@@ -127,7 +135,7 @@ def time_monolithic(torch, ops, cfg, t, steps, with_bwd=True):
     def step():
         ops.lh_forward(cfg, t["q"], t["k"], t["v"], bufs=bufs, y=y)
         if with_bwd:
-            ops.lh_backward(cfg, bufs, t["dy"], *dx)
+            ops.lh_backward(cfg, t["q"], t["k"], t["v"], bufs, t["dy"], *dx)
 
     step()
     torch.cuda.synchronize()
@@ -139,6 +147,27 @@ def time_monolithic(torch, ops, cfg, t, steps, with_bwd=True):
     torch.cuda.synchronize()
     del bufs
     return a.elapsed_time(b) / steps
+
+
+def time_dense(torch, ops, t, steps):
+    """This library's dense causal attention straight on the [B, N, H, D] token tensors (the
+    stage-2 dense-resumption call): forward, and forward + backward, with HIP events."""
+    q, k, v, dy = t["q"], t["k"], t["v"], t["dy"]
+    o, lse = ops.lh_attn_fwd(q, k, v, layout="bshd")
+    ops.lh_attn_bwd(q, k, v, o, lse, dy, layout="bshd")
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    fwd, bwd = [], []
+    for _ in range(steps):
+        ev[0].record()
+        o, lse = ops.lh_attn_fwd(q, k, v, layout="bshd")
+        ev[1].record()
+        ops.lh_attn_bwd(q, k, v, o, lse, dy, layout="bshd")
+        ev[2].record()
+        torch.cuda.synchronize()
+        fwd.append(ev[0].elapsed_time(ev[1]))
+        bwd.append(ev[1].elapsed_time(ev[2]))
+    return statistics.median(fwd), statistics.median(bwd)
 
 
 def cpu_baseline(w, x):
@@ -153,7 +182,7 @@ def cpu_baseline(w, x):
     except Exception:  # pragma: no cover
         cores = 1
     ocfg = O.Config(w.levels, w.pool, w.k, w.chunk,
-                    mode=O.DIRECT if w.mode == "direct" else O.REFINE)
+                    mode=O.DIRECT if w.mode == "direct" else O.REFINE, scorer=w.scorer)
     q, k, v, dy = (x[n][0, :, 0].astype(np.float64) for n in ("q", "k", "v", "dy"))
     t0 = time.perf_counter()
     _, st = O.head_forward(q, k, v, ocfg)
@@ -174,6 +203,8 @@ def main():
     ap.add_argument("--workload", default="lh-512k")
     ap.add_argument("--select", choices=("refine", "direct"), default="refine",
                     help="selection reading (the metric is quoted on refine)")
+    ap.add_argument("--scorer", choices=("k", "qk", "qkv"), default="k",
+                    help="score of a pooled entry (the metric is quoted on k)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention baseline")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
@@ -201,6 +232,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.select != w.mode:
         w = dataclasses.replace(w, name=f"{w.name}-{args.select}", mode=args.select)
+    if args.scorer != w.scorer:
+        w = dataclasses.replace(w, name=f"{w.name}-{args.scorer}", scorer=args.scorer)
     log(f"workload {w}")
     t0 = time.perf_counter()
     x = synth.workload_inputs(w, with_grad=True)
@@ -253,14 +286,19 @@ def main():
 
     dense = None
     if not args.no_dense:
-        dw = synth.Workload("dense-" + w.name, w.batch, w.n_tokens, w.heads, w.head_dim, w.dtype,
-                            1, w.pool, 0, w.chunk, w.seed, True)
-        dcfg = ops.config_for(dw)
-        log("timing the dense causal attention baseline (levels = 1, S = N)")
-        d_fb = time_monolithic(torch, ops, dcfg, t, 1)
-        d_f = time_monolithic(torch, ops, dcfg, t, 1, with_bwd=False)
-        dense = {"fwd_ms": round(d_f, 2), "fwd_bwd_ms": round(d_fb, 2),
-                 "speedup_fwd": round(d_f / mono_f, 2), "speedup_fwd_bwd": round(d_fb / mono_fb, 2)}
+        log("timing the dense causal attention on the token tensors (S = N)")
+        d_f, d_b = time_dense(torch, ops, t, 2)
+        dpairs = w.batch * w.heads * w.n_tokens * (w.n_tokens + 1) / 2
+        dfl_f, dfl_b = 2 * 2 * w.head_dim * dpairs, 5 * 2 * w.head_dim * dpairs
+        dense = {"fwd_ms": round(d_f, 2), "fwd_bwd_ms": round(d_f + d_b, 2),
+                 "speedup_fwd": round(d_f / mono_f, 2),
+                 "speedup_fwd_bwd": round((d_f + d_b) / mono_fb, 2),
+                 "roofline_fwd": {"bound": "mfma", "achieved": round(dfl_f / (d_f * 1e-3) / 1e12, 1),
+                                  "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(dfl_f / (d_f * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+                 "roofline_bwd": {"bound": "mfma", "achieved": round(dfl_b / (d_b * 1e-3) / 1e12, 1),
+                                  "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(dfl_b / (d_b * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}}
         log(f"dense: {dense}")
         torch.cuda.empty_cache()
 
@@ -271,14 +309,16 @@ def main():
         log(f"cpu baseline: {cpu}")
 
     out = {
-        "metric": METRIC, "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s/layer",
+        "metric": metric_name(w.n_tokens), "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s/layer",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_tokens": w.n_tokens, "heads": w.heads,
                    "head_dim": w.head_dim, "levels": w.levels, "pool": w.pool, "k": w.k,
                    "chunk": w.chunk, "gathered_len": info.gathered_len,
-                   "input_dtype": w.dtype, "seed": w.seed, "select": w.mode},
+                   "input_dtype": w.dtype, "seed": w.seed, "select": w.mode,
+                   "scorer": w.scorer},
         "roofline": roof,
         "cpu_baseline": cpu,
         "forward_tokens_per_s": round(tokens / (fwd_ms * 1e-3), 1),
@@ -286,7 +326,8 @@ def main():
         "monolithic_ms": {"fwd_bwd": round(mono_fb, 4), "fwd": round(mono_f, 4)},
         "hbm_stages": {"bytes": int(hbm_bytes), "ms": round(hbm_ms, 4),
                        "gbs": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9, 1),
-                       "frac": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                       "frac": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "bytes_per_token": round(hbm_bytes / tokens, 1)},
         "stages": stages,
         "dense_baseline": dense,
     }

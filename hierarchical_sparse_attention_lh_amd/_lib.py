@@ -45,47 +45,52 @@ class LhPlanInfo(ctypes.Structure):
     _fields_ = [
         ("level_size", _I64L), ("level_offset", _I64L), ("pooled_offset", _I64L),
         ("pyramid_total", ctypes.c_int64), ("pooled_rows", ctypes.c_int64),
-        ("k_eff", _I64L), ("n_chunks", _I64L), ("chunk_width", _I64L), ("sel_offset", _I64L),
+        ("k_eff", _I64L), ("n_chunks", _I64L), ("chunk_width", _I64L),
+        ("quota_base", _I64L), ("quota_rem", _I64L), ("sel_offset", _I64L),
         ("sel_total", ctypes.c_int64), ("gathered_len", ctypes.c_int64),
         ("gathered_pad", ctypes.c_int64),
         ("saved_gmap", ctypes.c_size_t), ("saved_inv", ctypes.c_size_t),
-        ("saved_q", ctypes.c_size_t), ("saved_k", ctypes.c_size_t), ("saved_v", ctypes.c_size_t),
-        ("saved_qt", ctypes.c_size_t), ("saved_kt", ctypes.c_size_t),
-        ("saved_vt", ctypes.c_size_t), ("saved_o", ctypes.c_size_t),
-        ("saved_lse", ctypes.c_size_t), ("saved_bytes", ctypes.c_size_t),
+        ("saved_pq", ctypes.c_size_t), ("saved_pk", ctypes.c_size_t), ("saved_pv", ctypes.c_size_t),
+        ("saved_o", ctypes.c_size_t), ("saved_lse", ctypes.c_size_t),
+        ("saved_bytes", ctypes.c_size_t),
         ("ws_forward_bytes", ctypes.c_size_t), ("ws_backward_bytes", ctypes.c_size_t),
         ("softmax_scale", ctypes.c_float),
     ]
 
 
-class LhGathered(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v", "qt", "kt", "vt")]
+_I64x3 = ctypes.c_int64 * 3
 
 
 class LhAttnDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("seq", ctypes.c_int64),
-                ("head_dim", ctypes.c_int64), ("scale", ctypes.c_float)]
+                ("head_dim", ctypes.c_int64), ("q_stride", _I64x3), ("k_stride", _I64x3),
+                ("v_stride", _I64x3), ("o_stride", _I64x3), ("causal", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
 
 
 P = ctypes.c_void_p
 _CFG = ctypes.POINTER(LhConfig)
+_DESC = ctypes.POINTER(LhAttnDesc)
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
 _SIGS = {
     "lh_plan": [_CFG, ctypes.POINTER(LhPlanInfo)],
     "lh_status_string": [ctypes.c_int],
-    "lh_pool_score": [_CFG, P, P, P, P, P, P, ctypes.c_int32, P, P],
+    "lh_pool_score": [_CFG, P, P, P, P, P, P, _I32, P, P],
     "lh_topk": [_CFG, P, P, P],
     "lh_build_map": [_CFG, P, P, P, P],
-    "lh_gather": [_CFG, P, P, P, P, P, P, ctypes.c_int32, P, ctypes.POINTER(LhGathered), P],
-    "lh_attn_fwd": [ctypes.POINTER(LhAttnDesc), P, P, P, P, P, P],
-    "lh_attn_bwd": [ctypes.POINTER(LhAttnDesc), P, P, P, P, P, P, P, P, P, P, P, P, P],
-    "lh_attn_bwd_dkdv": [ctypes.POINTER(LhAttnDesc), P, P, P, P, P, P, P, P, P, P, P, P, P],
-    "lh_attn_bwd_dq": [ctypes.POINTER(LhAttnDesc), P, P, P, P, P, P, P, P, P, P, P, P, P],
+    "lh_gather": [_CFG, P, P, P, P, P, P, _I32, P, P, P, P, P, P, P],
+    "lh_attn_fwd": [_DESC, P, P, P, P, P, P],
+    "lh_attn_ws_bytes": [_DESC, ctypes.POINTER(_SZ)],
+    "lh_attn_bwd": [_DESC, P, P, P, P, P, P, P, P, P, P, _SZ, P],
+    "lh_attn_fwd_mapped": [_CFG, P, P, P, P, P, P, P, P, P, P],
+    "lh_attn_bwd_mapped": [_CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, _I32, P],
     "lh_scatter": [_CFG, P, P, P, P],
-    "lh_scatter_bwd": [_CFG, P, P, P, P, P, P, P],
+    "lh_scatter_bwd": [_CFG, P, P, P, P, P, P],
     "lh_gather_pool_bwd": [_CFG, P, P, P, P, P, P, P, P],
-    "lh_forward": [_CFG, P, P, P, P, P, P, ctypes.c_size_t, P],
+    "lh_forward": [_CFG, P, P, P, P, P, P, _SZ, P],
     "lh_forward_noalloc": [_CFG, P, P, P, P, P, P],
-    "lh_backward": [_CFG, P, P, P, P, P, P, ctypes.c_size_t, P],
+    "lh_backward": [_CFG, P, P, P, P, P, P, P, P, P, _SZ, P],
 }
 EXPORTS = tuple(_SIGS)
 

@@ -135,6 +135,10 @@ void fill_plan(const lh_config* c, const Levels& L, lh_plan_info* info) {
     info->k_eff[l] = L.keff[l];
     info->n_chunks[l] = L.nchunk[l];
     info->chunk_width[l] = L.width[l];
+    if (L.nchunk[l] > 0) {
+      info->quota_base[l] = L.keff[l] / L.nchunk[l];
+      info->quota_rem[l] = L.keff[l] % L.nchunk[l];
+    }
     info->sel_offset[l] = L.soff[l];
   }
   info->pyramid_total = L.P;
@@ -151,27 +155,36 @@ void fill_plan(const lh_config* c, const Levels& L, lh_plan_info* info) {
     o = align256(o + bytes);
     return at;
   };
+  const size_t pooled = static_cast<size_t>(L.B * L.P1) * L.H * D * 2;
   info->saved_gmap = take(BH * Sp * 4);
   info->saved_inv = take(BH * L.P * 4);
-  info->saved_q = take(BH * Sp * D * 2);
-  info->saved_k = take(BH * Sp * D * 2);
-  info->saved_v = take(BH * Sp * D * 2);
-  info->saved_qt = take(BH * Sp * D * 2);
-  info->saved_kt = take(BH * Sp * D * 2);
-  info->saved_vt = take(BH * Sp * D * 2);
+  info->saved_pq = take(pooled);
+  info->saved_pk = take(pooled);
+  info->saved_pv = take(pooled);
   info->saved_o = take(BH * Sp * D * 4);
   info->saved_lse = take(BH * Sp * 4);
   info->saved_bytes = o;
-  const size_t pooled = align256(static_cast<size_t>(L.B * L.P1) * L.H * D * 2);
-  info->ws_forward_bytes = 3 * pooled + align256(BH * L.P * 4) + align256(BH * L.K * 4 + 4);
-  info->ws_backward_bytes = 2 * align256(BH * Sp * D * 2) + align256(BH * Sp * 4) +
+  if (c->dtype == LH_F32) {
+    // float32 layers keep the bf16 rounding of their token rows (the attention's level-0 rows)
+    info->saved_bytes += 3 * align256(static_cast<size_t>(L.B * L.N) * L.H * D * 2);
+  }
+  info->ws_forward_bytes = align256(BH * L.P * 4) + align256(BH * L.K * 4 + 4);
+  info->ws_backward_bytes = align256(BH * Sp * D * 2) + align256(BH * Sp * 4) +
                             3 * align256(BH * Sp * D * 4);
   info->softmax_scale = resolved_scale(c->softmax_scale, L.D);
 }
 
+// Offset of the bf16 token copies (which = 0, 1, 2 for Q, K, V) a float32 layer keeps at the
+// end of `saved`.
+size_t raw_copy_offset(const lh_plan_info& P, const Levels& L, int which) {
+  const size_t one = align256(static_cast<size_t>(L.B * L.N) * L.H * L.D * 2);
+  return align256(P.saved_lse + static_cast<size_t>(L.B * L.H) * P.gathered_pad * 4) +
+         which * one;
+}
+
 // Offsets of the backward workspace pieces.
 struct BwdWs {
-  size_t dog, dogt, delta, dq, dk, dv;
+  size_t dog, delta, dq, dk, dv;
 };
 BwdWs bwd_layout(const Levels& L) {
   const size_t BH = static_cast<size_t>(L.B * L.H), D = L.D;
@@ -179,7 +192,6 @@ BwdWs bwd_layout(const Levels& L) {
   BwdWs w;
   size_t o = 0;
   w.dog = o; o += align256(BH * Sp * D * 2);
-  w.dogt = o; o += align256(BH * Sp * D * 2);
   w.delta = o; o += align256(BH * Sp * 4);
   w.dq = o; o += align256(BH * Sp * D * 4);
   w.dk = o; o += align256(BH * Sp * D * 4);
@@ -218,12 +230,71 @@ lh_status scratch_address(void** out) {
   return LH_OK;
 }
 
+bool stride_ok(const int64_t st[3]) {
+  return st[0] >= 0 && st[1] >= 0 && st[2] >= 0 && st[0] % 8 == 0 && st[1] % 8 == 0 &&
+         st[2] % 8 == 0;
+}
+
 lh_status check_desc(const lh_attn_desc* d) {
   if (d == nullptr) return LH_ERR_NULL;
   if (d->batch < 1 || d->heads < 1 || d->seq < 1 || d->seq > kMaxAttnLen) return LH_ERR_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return LH_ERR_DTYPE;
   if (d->batch * d->heads * (lh::padded_len(d->seq) / 128) > 0x7fffffffLL) return LH_ERR_SHAPE;
+  if (!stride_ok(d->q_stride) || !stride_ok(d->k_stride) || !stride_ok(d->v_stride) ||
+      !stride_ok(d->o_stride))
+    return LH_ERR_ALIGN;
   return LH_OK;
+}
+
+// An attention call over strided rows.
+lh::AttnCall strided_call(const lh_attn_desc* d) {
+  lh::AttnCall c;
+  memset(&c, 0, sizeof(c));
+  c.B = d->batch;
+  c.H = d->heads;
+  c.S = d->seq;
+  c.D = static_cast<int32_t>(d->head_dim);
+  c.scale = resolved_scale(d->scale, c.D);
+  c.causal = d->causal != 0;
+  c.o_rows = static_cast<int32_t>(d->seq);
+  for (int i = 0; i < 3; ++i) {
+    c.q_stride[i] = d->q_stride[i];
+    c.k_stride[i] = d->k_stride[i];
+    c.v_stride[i] = d->v_stride[i];
+    c.o_stride[i] = d->o_stride[i];
+    c.do_stride[i] = d->o_stride[i];
+    c.g_stride[i] = d->o_stride[i];
+  }
+  return c;
+}
+
+// The layer's attention: causal, rows through gmap (L >= 2) or the token tensors themselves
+// (L = 1, the identity map), outputs in the padded gathered layout [B, H, Sp, D].
+lh::AttnCall layer_call(const Levels& L, float scale, const int32_t* gmap, const void* pq,
+                        const void* pk, const void* pv) {
+  lh::AttnCall c;
+  memset(&c, 0, sizeof(c));
+  c.B = L.B;
+  c.H = L.H;
+  c.S = L.S;
+  c.D = L.D;
+  c.scale = scale;
+  c.causal = 1;
+  const int64_t Sp = lh::padded_len(L.S);
+  c.o_rows = static_cast<int32_t>(Sp);
+  const int64_t tok[3] = {L.N * L.H * L.D, L.D, static_cast<int64_t>(L.H) * L.D};
+  const int64_t gat[3] = {L.H * Sp * L.D, Sp * L.D, L.D};
+  for (int i = 0; i < 3; ++i) {
+    c.q_stride[i] = c.k_stride[i] = c.v_stride[i] = tok[i];
+    c.o_stride[i] = c.do_stride[i] = c.g_stride[i] = gat[i];
+  }
+  c.mapped = L.L > 1;
+  c.lv = &L;
+  c.gmap = gmap;
+  c.pq = pq;
+  c.pk = pk;
+  c.pv = pv;
+  return c;
 }
 
 }  // namespace
@@ -291,83 +362,90 @@ lh_status lh_build_map(const lh_config* cfg, const int32_t* sel, int32_t* gmap, 
 
 lh_status lh_gather(const lh_config* cfg, const void* q, const void* k, const void* v,
                     const void* pq, const void* pk, const void* pv, int32_t pooled_dtype,
-                    const int32_t* gmap, const lh_gathered* out, lh_stream_t stream) {
+                    const int32_t* sel, int32_t* gmap, int32_t* inv, void* qg, void* kg,
+                    void* vg, lh_stream_t stream) {
   Levels L;
   LH_TRY(check_config(cfg, &L));
-  if (out == nullptr) return LH_ERR_NULL;
-  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(v)); LH_TRY(need(gmap));
+  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(v));
+  if (L.K > 0) LH_TRY(need(sel));
+  LH_TRY(need(gmap)); LH_TRY(need(inv));
   if (L.L > 1) { LH_TRY(need(pq)); LH_TRY(need(pk)); LH_TRY(need(pv)); }
-  LH_TRY(need(out->q)); LH_TRY(need(out->k)); LH_TRY(need(out->vt));
-  LH_TRY(maybe(out->v)); LH_TRY(maybe(out->qt)); LH_TRY(maybe(out->kt));
+  LH_TRY(need(qg)); LH_TRY(need(kg)); LH_TRY(need(vg));
   if (pooled_dtype != LH_BF16 && pooled_dtype != LH_F32) return LH_ERR_DTYPE;
+  auto st = static_cast<hipStream_t>(stream);
+  LH_TRY(launched(lh::launch_build_map(L, sel, gmap, inv, st), st));
   const void* x[3] = {q, k, v};
   const void* px[3] = {pq, pk, pv};
-  void* const rows[3] = {out->q, out->k, out->v};
-  void* const trans[3] = {out->qt, out->kt, out->vt};
-  auto st = static_cast<hipStream_t>(stream);
+  void* const rows[3] = {qg, kg, vg};
   return launched(lh::launch_gather(L, cfg->dtype == LH_F32, x, px, pooled_dtype == LH_F32, gmap,
-                                    rows, trans, st), st);
+                                    rows, st), st);
 }
 
-lh_status lh_attn_fwd(const lh_attn_desc* desc, const void* q, const void* k, const void* vt,
+lh_status lh_attn_fwd(const lh_attn_desc* desc, const void* q, const void* k, const void* v,
                       float* o, float* lse, lh_stream_t stream) {
   LH_TRY(check_desc(desc));
-  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(vt)); LH_TRY(need(o)); LH_TRY(need(lse));
+  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(v)); LH_TRY(need(o)); LH_TRY(need(lse));
   auto st = static_cast<hipStream_t>(stream);
-  return launched(lh::launch_attn_fwd(desc->batch, desc->heads, desc->seq, desc->head_dim,
-                                      resolved_scale(desc->scale, desc->head_dim), q, k, vt, o,
-                                      lse, st), st);
+  const lh::AttnCall c = strided_call(desc);
+  return launched(lh::launch_attn_fwd2(c, q, k, v, o, lse, st), st);
+}
+
+lh_status lh_attn_ws_bytes(const lh_attn_desc* desc, size_t* bytes) {
+  LH_TRY(check_desc(desc));
+  if (bytes == nullptr) return LH_ERR_NULL;
+  *bytes = align256(static_cast<size_t>(desc->batch * desc->heads) *
+                    static_cast<size_t>(lh::padded_len(desc->seq)) * 4);
+  return LH_OK;
 }
 
 lh_status lh_attn_bwd(const lh_attn_desc* desc, const void* q, const void* k, const void* v,
-                      const void* qt, const void* kt, const float* lse, const float* delta,
-                      const void* dout, const void* doutt, float* dq, float* dk, float* dv,
-                      lh_stream_t stream) {
+                      const float* o, const float* lse, const void* dout, float* dq, float* dk,
+                      float* dv, void* ws, size_t ws_bytes, lh_stream_t stream) {
   LH_TRY(check_desc(desc));
-  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(v)); LH_TRY(need(qt)); LH_TRY(need(kt));
-  LH_TRY(need(lse)); LH_TRY(need(delta)); LH_TRY(need(dout)); LH_TRY(need(doutt));
-  LH_TRY(need(dq)); LH_TRY(need(dk)); LH_TRY(need(dv));
+  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(v)); LH_TRY(need(o)); LH_TRY(need(lse));
+  LH_TRY(need(dout)); LH_TRY(need(dq)); LH_TRY(need(dk)); LH_TRY(need(dv)); LH_TRY(need(ws));
+  size_t want = 0;
+  LH_TRY(lh_attn_ws_bytes(desc, &want));
+  if (ws_bytes < want) return LH_ERR_WORKSPACE;
   auto st = static_cast<hipStream_t>(stream);
-  return launched(lh::launch_attn_bwd(desc->batch, desc->heads, desc->seq, desc->head_dim,
-                                      resolved_scale(desc->scale, desc->head_dim), q, k, v, qt,
-                                      kt, lse, delta, dout, doutt, dq, dk, dv, st), st);
+  const lh::AttnCall c = strided_call(desc);
+  float* delta = static_cast<float*>(ws);
+  LH_TRY(launched(lh::launch_attn_delta(c, dout, o, delta, st), st));
+  return launched(lh::launch_attn_bwd2(3, c, q, k, v, dout, lse, delta, dq, dk, dv, st), st);
 }
 
-lh_status lh_attn_bwd_dkdv(const lh_attn_desc* desc, const void* q, const void* k,
-                           const void* v, const void* qt, const void* kt, const float* lse,
-                           const float* delta, const void* dout, const void* doutt, float* dq,
-                           float* dk, float* dv, lh_stream_t stream) {
-  (void)kt;
-  (void)dq;
-  LH_TRY(check_desc(desc));
-  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(v)); LH_TRY(need(qt)); LH_TRY(need(lse));
-  LH_TRY(need(delta)); LH_TRY(need(dout)); LH_TRY(need(doutt)); LH_TRY(need(dk));
-  LH_TRY(need(dv));
+lh_status lh_attn_fwd_mapped(const lh_config* cfg, const void* q, const void* k, const void* v,
+                             const void* pq, const void* pk, const void* pv,
+                             const int32_t* gmap, float* og, float* lse, lh_stream_t stream) {
+  Levels L;
+  LH_TRY(check_config(cfg, &L));
+  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(v)); LH_TRY(need(gmap)); LH_TRY(need(og));
+  LH_TRY(need(lse));
+  if (L.L > 1) { LH_TRY(need(pq)); LH_TRY(need(pk)); LH_TRY(need(pv)); }
   auto st = static_cast<hipStream_t>(stream);
-  return launched(lh::launch_attn_bwd_pass(1, desc->batch, desc->heads, desc->seq,
-                                           desc->head_dim,
-                                           resolved_scale(desc->scale, desc->head_dim), q, k, v,
-                                           qt, nullptr, lse, delta, dout, doutt, nullptr, dk, dv,
-                                           st), st);
+  const lh::AttnCall c =
+      layer_call(L, resolved_scale(cfg->softmax_scale, L.D), gmap, pq, pk, pv);
+  return launched(lh::launch_attn_fwd2(c, q, k, v, og, lse, st), st);
 }
 
-lh_status lh_attn_bwd_dq(const lh_attn_desc* desc, const void* q, const void* k, const void* v,
-                         const void* qt, const void* kt, const float* lse, const float* delta,
-                         const void* dout, const void* doutt, float* dq, float* dk, float* dv,
-                         lh_stream_t stream) {
-  (void)qt;
-  (void)doutt;
-  (void)dk;
-  (void)dv;
-  LH_TRY(check_desc(desc));
-  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(v)); LH_TRY(need(kt)); LH_TRY(need(lse));
-  LH_TRY(need(delta)); LH_TRY(need(dout)); LH_TRY(need(dq));
+lh_status lh_attn_bwd_mapped(const lh_config* cfg, const void* q, const void* k, const void* v,
+                             const void* pq, const void* pk, const void* pv,
+                             const int32_t* gmap, const float* lse, const float* delta,
+                             const void* dog, float* dqg, float* dkg, float* dvg, int32_t passes,
+                             lh_stream_t stream) {
+  Levels L;
+  LH_TRY(check_config(cfg, &L));
+  if (passes < 1 || passes > 3) return LH_ERR_UNSUPPORTED;
+  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(v)); LH_TRY(need(gmap)); LH_TRY(need(lse));
+  LH_TRY(need(delta)); LH_TRY(need(dog));
+  if (L.L > 1) { LH_TRY(need(pq)); LH_TRY(need(pk)); LH_TRY(need(pv)); }
+  if (passes & 1) { LH_TRY(need(dkg)); LH_TRY(need(dvg)); }
+  if (passes & 2) LH_TRY(need(dqg));
   auto st = static_cast<hipStream_t>(stream);
-  return launched(lh::launch_attn_bwd_pass(2, desc->batch, desc->heads, desc->seq,
-                                           desc->head_dim,
-                                           resolved_scale(desc->scale, desc->head_dim), q, k, v,
-                                           nullptr, kt, lse, delta, dout, nullptr, dq, nullptr,
-                                           nullptr, st), st);
+  const lh::AttnCall c =
+      layer_call(L, resolved_scale(cfg->softmax_scale, L.D), gmap, pq, pk, pv);
+  return launched(lh::launch_attn_bwd2(passes, c, q, k, v, dog, lse, delta, dqg, dkg, dvg, st),
+                  st);
 }
 
 lh_status lh_scatter(const lh_config* cfg, const int32_t* inv, const float* og, void* y,
@@ -380,15 +458,13 @@ lh_status lh_scatter(const lh_config* cfg, const int32_t* inv, const float* og, 
 }
 
 lh_status lh_scatter_bwd(const lh_config* cfg, const int32_t* gmap, const float* og,
-                         const void* dy, void* dog, void* dogt, float* delta,
-                         lh_stream_t stream) {
+                         const void* dy, void* dog, float* delta, lh_stream_t stream) {
   Levels L;
   LH_TRY(check_config(cfg, &L));
-  LH_TRY(need(gmap)); LH_TRY(need(og)); LH_TRY(need(dy)); LH_TRY(need(dog));
-  LH_TRY(need(dogt)); LH_TRY(need(delta));
+  LH_TRY(need(gmap)); LH_TRY(need(og)); LH_TRY(need(dy)); LH_TRY(need(dog)); LH_TRY(need(delta));
   auto st = static_cast<hipStream_t>(stream);
-  return launched(lh::launch_scatter_bwd(L, cfg->dtype == LH_F32, gmap, og, dy, dog, dogt, delta,
-                                         st), st);
+  return launched(lh::launch_scatter_bwd(L, cfg->dtype == LH_F32, gmap, og, dy, dog, delta, st),
+                  st);
 }
 
 lh_status lh_gather_pool_bwd(const lh_config* cfg, const int32_t* inv, const float* dqg,
@@ -413,13 +489,11 @@ lh_status forward_body(const lh_config* cfg, const Levels& L, const lh_plan_info
                        void* ws, lh_stream_t stream) {
   auto st = static_cast<hipStream_t>(stream);
   const int32_t f32 = cfg->dtype == LH_F32;
-
-  const size_t pooled = align256(static_cast<size_t>(L.B * L.P1) * L.H * L.D * 2);
-  void* pq = at(ws, 0);
-  void* pk = at(ws, pooled);
-  void* pv = at(ws, 2 * pooled);
-  float* scores = reinterpret_cast<float*>(at(ws, 3 * pooled));
-  int32_t* sel = reinterpret_cast<int32_t*>(at(ws, 3 * pooled + align256(L.B * L.H * L.P * 4)));
+  void* pq = at(saved, P.saved_pq);
+  void* pk = at(saved, P.saved_pk);
+  void* pv = at(saved, P.saved_pv);
+  float* scores = reinterpret_cast<float*>(ws);
+  int32_t* sel = reinterpret_cast<int32_t*>(at(ws, align256(L.B * L.H * L.P * 4)));
   int32_t* gmap = reinterpret_cast<int32_t*>(at(saved, P.saved_gmap));
   int32_t* inv = reinterpret_cast<int32_t*>(at(saved, P.saved_inv));
   float* og = reinterpret_cast<float*>(at(saved, P.saved_o));
@@ -428,13 +502,17 @@ lh_status forward_body(const lh_config* cfg, const Levels& L, const lh_plan_info
   LH_TRY(launched(lh::launch_pool_score(L, f32, q, k, v, pq, pk, pv, 0, scores, st), st));
   LH_TRY(launched(lh::launch_topk(L, scores, sel, st), st));
   LH_TRY(launched(lh::launch_build_map(L, sel, gmap, inv, st), st));
-  const void* x[3] = {q, k, v};
-  const void* px[3] = {pq, pk, pv};
-  void* const rows[3] = {at(saved, P.saved_q), at(saved, P.saved_k), at(saved, P.saved_v)};
-  void* const trans[3] = {at(saved, P.saved_qt), at(saved, P.saved_kt), at(saved, P.saved_vt)};
-  LH_TRY(launched(lh::launch_gather(L, f32, x, px, 0, gmap, rows, trans, st), st));
-  LH_TRY(launched(lh::launch_attn_fwd(L.B, L.H, L.S, L.D, P.softmax_scale, rows[0], rows[1],
-                                      trans[2], og, lse, st), st));
+  const void* rows[3] = {q, k, v};
+  if (f32) {  // the attention reads bf16 token rows: round the float32 inputs once
+    for (int i = 0; i < 3; ++i) {
+      void* copy = at(saved, raw_copy_offset(P, L, i));
+      LH_TRY(launched(lh::launch_to_bf16(static_cast<const float*>(rows[i]), copy,
+                                         L.B * L.N * L.H * L.D, st), st));
+      rows[i] = copy;
+    }
+  }
+  const lh::AttnCall c = layer_call(L, P.softmax_scale, gmap, pq, pk, pv);
+  LH_TRY(launched(lh::launch_attn_fwd2(c, rows[0], rows[1], rows[2], og, lse, st), st));
   return launched(lh::launch_scatter(L, f32, inv, og, y, st), st);
 }
 
@@ -467,10 +545,12 @@ lh_status lh_forward_noalloc(const lh_config* cfg, const void* q, const void* k,
   return forward_body(cfg, L, P, q, k, v, y, saved, ws, stream);
 }
 
-lh_status lh_backward(const lh_config* cfg, const void* saved, const void* dy, void* dq,
-                      void* dk, void* dv, void* ws, size_t ws_bytes, lh_stream_t stream) {
+lh_status lh_backward(const lh_config* cfg, const void* q, const void* k, const void* v,
+                      const void* saved, const void* dy, void* dq, void* dk, void* dv, void* ws,
+                      size_t ws_bytes, lh_stream_t stream) {
   Levels L;
   LH_TRY(check_config(cfg, &L));
+  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(v));
   LH_TRY(need(saved)); LH_TRY(need(dy)); LH_TRY(need(dq)); LH_TRY(need(dk)); LH_TRY(need(dv));
   LH_TRY(need(ws));
   lh_plan_info P;
@@ -484,17 +564,19 @@ lh_status lh_backward(const lh_config* cfg, const void* saved, const void* dy, v
   const float* og = reinterpret_cast<const float*>(at(saved, P.saved_o));
   const float* lse = reinterpret_cast<const float*>(at(saved, P.saved_lse));
   void* dog = at(ws, w.dog);
-  void* dogt = at(ws, w.dogt);
   float* delta = reinterpret_cast<float*>(at(ws, w.delta));
   float* dqg = reinterpret_cast<float*>(at(ws, w.dq));
   float* dkg = reinterpret_cast<float*>(at(ws, w.dk));
   float* dvg = reinterpret_cast<float*>(at(ws, w.dv));
+  const void* rows[3] = {q, k, v};
+  if (f32)  // the bf16 token rows lh_forward kept
+    for (int i = 0; i < 3; ++i) rows[i] = at(saved, raw_copy_offset(P, L, i));
 
-  LH_TRY(launched(lh::launch_scatter_bwd(L, f32, gmap, og, dy, dog, dogt, delta, st), st));
-  LH_TRY(launched(lh::launch_attn_bwd(L.B, L.H, L.S, L.D, P.softmax_scale, at(saved, P.saved_q),
-                                      at(saved, P.saved_k), at(saved, P.saved_v),
-                                      at(saved, P.saved_qt), at(saved, P.saved_kt), lse, delta, dog,
-                                      dogt, dqg, dkg, dvg, st), st));
+  LH_TRY(launched(lh::launch_scatter_bwd(L, f32, gmap, og, dy, dog, delta, st), st));
+  const lh::AttnCall c = layer_call(L, P.softmax_scale, gmap, at(saved, P.saved_pq),
+                                    at(saved, P.saved_pk), at(saved, P.saved_pv));
+  LH_TRY(launched(lh::launch_attn_bwd2(3, c, rows[0], rows[1], rows[2], dog, lse, delta, dqg,
+                                       dkg, dvg, st), st));
   return launched(lh::launch_gather_pool_bwd(L, f32, inv, dqg, dkg, dvg, dq, dk, dv, st), st);
 }
 

@@ -1,0 +1,1315 @@
+// Causal softmax attention over the gathered sequence and its backward: the layer's one
+// dense contraction.
+//
+// [WS] wispaper.ai, "Lighthouse Attention：预训练长文本的高速公路，训练提速 21 倍且无损恢复",
+// section "核心方法：金字塔池化与“外部选择”", item 3, and [HE] news.hamidun.com, "Nous Research
+// introduced Lighthouse Attention to accelerate LLM training", section "How Lighthouse
+// Attention Works": the selected entries form a dense causal subsequence that goes through
+// ordinary scaled dot-product attention.  [EN] encorp.ai, "Услуги по внедряване на AI задават
+// правилния въпрос за Lighthouse Attention", section "Как four-stage pipeline остава бърз, без
+// да чупи градиентите?": gradients reach Q, K and V through that attention (the selection has
+// none).  The pages call a stock FlashAttention kernel on another vendor's GPU; these are this
+// library's own kernels for gfx950.
+//
+// Forward: O = softmax(scale Q K^T + causal mask) V, with the base-2 log-sum-exp per row.
+// Backward, with P recomputed from the saved log-sum-exp and Delta = rowsum(dO * O):
+//   dV = P^T dO;  dP = dO V^T;  dS = P * (dP - Delta);  dQ = scale dS K;  dK = scale dS^T Q.
+//
+// Where rows come from.  A row of Q, K or V is read where it lives:
+//   * strided: row s of head (b, h) at base + b*sb + h*sh + s*ss (dense attention straight
+//     on a [B, N, H, D] tensor, or on a gathered [B, H, S, D] copy);
+//   * mapped: row s of head (b, h) is pyramid entry id = gmap[b, h, s], a raw token row of the
+//     input (id < N) or a pooled row (id - N) of the pooled levels -- the gathered sequence is
+//     never materialised.  The ids of the tile after next are brought into LDS by a direct
+//     load, so each staging load knows its address without waiting on memory.
+// Tiles are staged with gfx950 direct global->LDS loads (no VGPR round trip) into row-major,
+// XOR-swizzled LDS tiles, double-buffered.  Every MFMA operand that needs a tile transposed
+// (V^T in the forward, dO^T and Q^T in the key pass, K^T in the query pass) is read from the
+// row tile with two ds_read_b64_tr_b16 transposing LDS reads, so no transposed copy of any
+// tensor exists.  The swizzle keeps both read kinds free of bank conflicts: sixteen rows at
+// one logical 16-byte chunk, and four rows x 64 bytes for a transposing read, each land in
+// distinct bank groups.
+//
+// Matrix products: v_mfma_f32_32x32x16_bf16 (lane layouts in lh_mfma.h).  Scores are
+// computed with the key index as the C row (forward, query pass: S^T = K Q^T) or column (key
+// pass: S = Q K^T) so that P and dS leave the C registers as the next product's B operand.
+// P and dS enter every product as a bf16 hi/lo pair (about 16 significant bits): with single
+// bf16 operands the gradients' error under cancellation exceeds their own bf16 output
+// rounding several times over.  The forward row sum is Kahan-compensated per tile (Delta
+// amplifies any error in O).  The backward is deterministic: a key pass writes dK and dV, a
+// query pass recomputes S and dP and writes dQ; no atomics.
+#include <type_traits>
+
+#include "lh_internal.h"
+#include "lh_mfma.h"
+
+namespace lh {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSlack = 8.0f;  // base-2 growth of the row max tolerated before a rescale
+
+// ------------------------------------------------------------------------ LDS layout
+__device__ __forceinline__ constexpr int bitrev3(int x) {
+  return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+}
+
+// XOR key of LDS tile row r (rows of D bf16).  D = 64: a 128-byte row fills half a 256-byte
+// bank line, rows 2j and 2j + 1 share key bitrev3(j mod 8); D = 128: a row fills a line and
+// gets ((r mod 4) << 2) | ((r / 4) mod 4).  Rows 16 t + r and r share a key (so does 32 m + r).
+template <int D>
+__device__ __forceinline__ int rkey(int r) {
+  if constexpr (D == 64)
+    return bitrev3((r >> 1) & 7);
+  else
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+
+// Byte offset of logical 16-byte chunk 2j + hl of row lq: one per-lane value per k step;
+// row 32 m + lq of any tile of this row length is 64 D m bytes further.
+template <int D>
+__device__ __forceinline__ uint32_t op_off(int lq, int hl, int j) {
+  return static_cast<uint32_t>(lq * D * 2 + (((2 * j + hl) ^ rkey<D>(lq)) << 4));
+}
+
+// Byte offset (within a 16-row chunk) of one of the two transposing reads (sec 0: rows 0-7,
+// sec 1: rows 8-15) that give lane l the elements X[16 t + k][32 db + l % 32] for its 8 k
+// values, in the k order in which c_to_op2 hands out the C registers of the other operand.
+// ds_read_b64_tr_b16 hands output lane i of each group of 16 lanes element (i mod 4) of the
+// 8-byte pieces addressed by lanes 4j + i / 4 (j = 0..3); so source lane s of group g
+// addresses row 4 (g / 2) + s / 4 (+ 8 for sec 1), columns 32 db + 16 (g mod 2) + 4 (s mod 4).
+template <int D>
+__device__ __forceinline__ uint32_t tr_off(int lane, int db, int sec) {
+  const int g = lane >> 4, s = lane & 15;
+  const int r = (g >> 1) * 4 + (s >> 2) + 8 * sec;
+  const int col = 32 * db + 16 * (g & 1) + 4 * (s & 3);
+  return static_cast<uint32_t>(r * D * 2 + (((col >> 3) ^ rkey<D>(r)) << 4) + ((col & 7) << 1));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ v4i16 ds_tr16(const uint16_t* tile, uint32_t off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)((lds_char*)(const_cast<uint16_t*>(tile)) + off));
+}
+
+// The transposed operand X^T (d rows, 16 k values of chunk t) from a row tile X.
+__device__ __forceinline__ bf16x8 tr_op(const uint16_t* tile, uint32_t off0, uint32_t off1) {
+  const v4i16 a = ds_tr16(tile, off0), b = ds_tr16(tile, off1);
+  const v8i16 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// ------------------------------------------------------------------------ row sources
+// Element (b, h, s, d) of a strided operand is x[b sb + h sh + s ss + d].  Mapped operands
+// (n0 = N) read row id of head (b, h) from x when id < n0, else row id - n0 of px (batch
+// stride psb, same head and row strides).  Strided operands have n0 beyond every id.
+struct RowSrc {
+  const uint16_t* x;
+  const uint16_t* px;
+  int64_t sb, sh, ss, psb, n0;
+};
+
+struct HeadRows {
+  const uint16_t* x;
+  const uint16_t* p;
+  int64_t ss, n0;
+};
+
+__device__ __forceinline__ HeadRows head_rows(const RowSrc& r, int64_t b, int64_t h) {
+  HeadRows o;
+  o.x = r.x + b * r.sb + h * r.sh;
+  o.p = r.px != nullptr ? r.px + b * r.psb + h * r.sh : nullptr;
+  o.ss = r.ss;
+  o.n0 = r.n0;
+  return o;
+}
+
+__device__ __forceinline__ const uint16_t* row_ptr(const HeadRows& hr, int64_t id) {
+  return id < hr.n0 ? hr.x + id * hr.ss : hr.p + (id - hr.n0) * hr.ss;
+}
+
+// Rows staged per lane for a ROWS x D tile (256 threads, 16 bytes per lane per load).
+template <int ROWS, int D>
+struct Tile {
+  static constexpr int CPR = D / 8;
+  static constexpr int LOADS = ROWS * CPR / 256;
+  static_assert(ROWS * CPR % 256 == 0, "tile must be a whole number of loads per thread");
+  // tile row of this lane's i-th load
+  __device__ static __forceinline__ int row(int i, int wave, int lane) {
+    return ((i * 4 + wave) * 64 + lane) / CPR;
+  }
+};
+
+// Row ids of the rows this lane stages for the tile starting at position row0: mapped ids
+// come from the LDS ring slot `ring` (padding slots hold -1 and read row 0); strided
+// positions past the sequence are clamped to its last row (their results are masked).
+template <int ROWS, int D, bool MAPPED>
+__device__ __forceinline__ void tile_ids(const int32_t* ring, int row0, int S, int wave, int lane,
+                                         int (&id)[Tile<ROWS, D>::LOADS]) {
+#pragma unroll
+  for (int i = 0; i < Tile<ROWS, D>::LOADS; ++i) {
+    const int r = Tile<ROWS, D>::row(i, wave, lane);
+    if constexpr (MAPPED)
+      id[i] = max(ring[r], 0);
+    else
+      id[i] = min(row0 + r, S - 1);
+  }
+}
+
+// Direct global->LDS loads of ROWS rows into a swizzled tile: each wave instruction fills 1 KB
+// of contiguous LDS, so lane l fetches the global chunk that belongs at LDS chunk base + l.
+template <int ROWS, int D>
+__device__ __forceinline__ void stage_rows(const HeadRows& hr, const int (&id)[Tile<ROWS, D>::LOADS],
+                                           uint16_t* lds, int wave, int lane) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int i = 0; i < Tile<ROWS, D>::LOADS; ++i) {
+    const int base = (i * 4 + wave) * 64;
+    const int r = (base + lane) / CPR, pc = (base + lane) % CPR;
+    const uint16_t* g = row_ptr(hr, id[i]) + ((pc ^ rkey<D>(r)) << 3);
+    __builtin_amdgcn_global_load_lds(g, lds + base * 8, 16, 0, 0);
+  }
+}
+
+// n (<= 64) int32 / float values into LDS with one direct load (4 bytes per lane).
+__device__ __forceinline__ void stage_words(const void* g, void* lds, int lane, int n) {
+  if (lane < n) {
+    uint32_t boff = 4u * lane;
+    asm volatile("" : "+v"(boff));
+    __builtin_amdgcn_global_load_lds(static_cast<const char*>(g) + boff, lds, 4, 0, 0);
+  }
+}
+
+// ------------------------------------------------------------------------ forward
+struct FwdArgs {
+  RowSrc q, k, v;
+  const int32_t* gmap;        // mapped: [B*H, Sp] pyramid ids, -1 for padding
+  float* o;                   // O rows at o + b osb + h osh + s oss
+  int64_t osb, osh, oss;
+  float* lse;                 // [B*H, Sp], base 2
+  int64_t BH;
+  int H, S, Sp, o_rows, causal;
+  float sl2;                  // scale * log2(e)
+};
+
+template <int D, bool PIPE, bool MAPPED>
+__device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
+  constexpr int BM = 128, BN = 64;
+  using KT = Tile<BN, D>;
+  constexpr int NL = KT::LOADS;
+  __shared__ __attribute__((aligned(16))) uint16_t ks0[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t ks1[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs0[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs1[BN * D];
+  __shared__ __attribute__((aligned(16))) int32_t idr[4][BN];
+
+  const int S = a.S, Sp = a.Sp;
+  const int nqt = Sp / BM;
+  const int64_t item = xcd_item(blockIdx.x, a.BH * nqt);
+  const int64_t bh = item / nqt;
+  const int qt = nqt - 1 - static_cast<int>(item % nqt);  // far-from-diagonal (heavy) first
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, lq = lane & 31;
+  const int q0 = qt * BM;
+  const int qw = q0 + wave * 32;
+  const int myq = qw + lq;
+  const HeadRows hq = head_rows(a.q, b, h), hk = head_rows(a.k, b, h), hv = head_rows(a.v, b, h);
+  const int32_t* gm = MAPPED ? a.gmap + bh * Sp : nullptr;
+  const float sl2 = a.sl2;
+  const bool causal = a.causal != 0;
+
+  bf16x8 qreg[D / 16];
+  {
+    const int qid = MAPPED ? max(gm[myq], 0) : min(myq, S - 1);
+    const uint16_t* qr = row_ptr(hq, qid);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = ld_op16(qr + 16 * kk + hl * 8);
+  }
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
+  float m_run = -INFINITY, l_run = 0.f, l_cmp = 0.f;
+
+  const int kend = causal ? (S < q0 + BM ? S : q0 + BM) : S;
+  const int nkt = (kend + BN - 1) / BN;
+
+  // per-lane LDS byte offsets: K rows (16-byte operand reads), V^T (transposing reads)
+  uint32_t toff[D / 32][2];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) toff[db][sec] = tr_off<D>(lane, db, sec);
+
+  auto load_ids = [&](int t) {
+    if constexpr (MAPPED)
+      if (wave == 0 && t < nkt) stage_words(gm + t * BN, idr[t & 3], lane, BN);
+  };
+  auto ids_of = [&](int t, int (&id)[NL]) { tile_ids<BN, D, MAPPED>(idr[t & 3], t * BN, S, wave, lane, id); };
+
+  // S^T of one key tile: 32 keys x 32 queries per C block, two blocks.
+  auto scores = [&](f32x16 (&sacc)[2], auto bufc) {
+    const uint16_t* ksb = decltype(bufc)::value ? ks1 : ks0;
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+      sacc[b2] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        sacc[b2] = mfma32(lds_at(ksb, b2 * 64 * D + op_off<D>(lq, hl, kk)), qreg[kk], sacc[b2]);
+    }
+  };
+
+  auto mask = [&](int t, f32x16 (&sacc)[2]) {
+    const int k0 = t * BN;
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + b2 * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+        if ((causal && key > myq) || key >= S) sacc[b2][r] = -INFINITY;
+      }
+  };
+
+  // Online softmax of score tile t and its P V^T product, with the score product of tile t+1
+  // (into nxt, from K buffer !odd) woven into the same instruction stream: short chunks of one
+  // MFMA plus some vector work, fixed by scheduling barriers, so one wave's vector work runs
+  // beside the other wave's MFMAs.
+  auto soft_pv = [&](auto masked, int t, f32x16 (&sacc)[2], f32x16 (&nxt)[2], auto par) {
+    constexpr bool odd = decltype(par)::value;
+    const uint16_t* vsb = odd ? vs1 : vs0;
+    const uint16_t* ksn = odd ? ks0 : ks1;
+    bf16x8 ka[2][D / 16], va[4][D / 32];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) ka[b2][kk] = lds_at(ksn, b2 * 64 * D + op_off<D>(lq, hl, kk));
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        va[t4][db] = tr_op(vsb, t4 * 32 * D + toff[db][0], t4 * 32 * D + toff[db][1]);
+    if constexpr (decltype(masked)::value) mask(t, sacc);
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[b2][r]);
+    mx = pair_max(mx) * sl2;
+    const bool grow = mx > m_run + kSlack;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      l_run *= alpha;
+      l_cmp *= alpha;
+      m_run = m_new;
+    }
+    constexpr int NS = 2 * (D / 16);  // score MFMAs per tile
+    constexpr int EPC = 32 / NS;       // exponentials per chunk
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) nxt[b2] = zero16();
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int kk = i >> 1, b2 = i & 1;
+      nxt[b2] = mfma32(ka[b2][kk], qreg[kk], nxt[b2]);
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) {
+        const int e = i * EPC + u, eb = e >> 4, er = e & 15;
+        sacc[eb][er] = __builtin_amdgcn_exp2f(fmaf(sacc[eb][er], sl2, -m_run));
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2 * EPC, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bf16x8 ph[4], pl[4];
+    c_to_op2(sacc[0], 0, ph[0], pl[0]);
+    float part[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[r] = sacc[0][r] + sacc[1][r];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32(va[t4][db], pl[t4], oacc[db]);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32(va[t4][db], ph[t4], oacc[db]);
+      if (t4 < 3) c_to_op2(sacc[(t4 + 1) >> 1], (t4 + 1) & 1, ph[t4 + 1], pl[t4 + 1]);
+      if (t4 == 0) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) part[r] += part[r + 8];
+      } else if (t4 == 1) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[r] += part[r + 4];
+      } else if (t4 == 2) {
+        part[0] += part[2];
+        part[1] += part[3];
+        part[0] += part[1];
+      } else {
+        const float yk = part[0] - l_cmp;
+        const float tk = l_run + yk;
+        l_cmp = (tk - l_run) - yk;
+        l_run = tk;
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * (D / 32); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Pipelined step t: LDS holds K(t+1) and V(t); K(t+2) and V(t+1) are loaded into the
+  // buffers freed by step t-1, the ids of tile t+3 into the ring.  The ids are read from LDS
+  // before this step issues any load, so no read waits on a load still in flight.
+  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto par) {
+    constexpr bool odd = decltype(par)::value;
+    int idk[NL], idv[NL];
+    const bool sk = t + 2 < nkt, sv = t + 1 < nkt;
+    if (sk) ids_of(t + 2, idk);
+    if (sv) ids_of(t + 1, idv);
+    load_ids(t + 3);
+    if (sk) stage_rows<BN, D>(hk, idk, odd ? ks1 : ks0, wave, lane);
+    if (sv) stage_rows<BN, D>(hv, idv, odd ? vs0 : vs1, wave, lane);
+    const int k0 = t * BN;
+    if ((causal && k0 + BN - 1 > qw) || k0 + BN > S)
+      soft_pv(std::true_type{}, t, cur, nxt, par);
+    else
+      soft_pv(std::false_type{}, t, cur, nxt, par);
+    wait_vmem();
+    __syncthreads();
+  };
+
+  // Plain tile (D = 128, two waves per SIMD): S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto plain_tile = [&](auto masked, int t, auto bufc) {
+    constexpr bool B1 = decltype(bufc)::value;
+    const uint16_t* ksb = B1 ? ks1 : ks0;
+    const uint16_t* vsb = B1 ? vs1 : vs0;
+    f32x16 sacc[2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) sacc[b2] = zero16();
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+        sacc[b2] = mfma32(lds_at(ksb, b2 * 64 * D + op_off<D>(lq, hl, kk)), qreg[kk], sacc[b2]);
+    if constexpr (decltype(masked)::value) mask(t, sacc);
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[b2][r]);
+    mx = pair_max(mx) * sl2;
+    const bool grow = mx > m_run + kSlack;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      l_run *= alpha;
+      l_cmp *= alpha;
+      m_run = m_new;
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sacc[b2][r] = __builtin_amdgcn_exp2f(fmaf(sacc[b2][r], sl2, -m_run));
+    float part[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[r] = sacc[0][r] + sacc[1][r];
+#pragma unroll
+    for (int w2 = 8; w2 >= 1; w2 >>= 1)
+#pragma unroll
+      for (int r = 0; r < w2; ++r) part[r] += part[r + w2];
+    const float yk = part[0] - l_cmp;
+    const float tk = l_run + yk;
+    l_cmp = (tk - l_run) - yk;
+    l_run = tk;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      bf16x8 ph, pl;
+      c_to_op2(sacc[t4 >> 1], t4 & 1, ph, pl);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 av = tr_op(vsb, t4 * 32 * D + toff[db][0], t4 * 32 * D + toff[db][1]);
+        oacc[db] = mfma32(av, pl, oacc[db]);
+        oacc[db] = mfma32(av, ph, oacc[db]);
+      }
+    }
+  };
+
+  auto plain_step = [&](int t, auto bufc) {
+    constexpr bool B1 = decltype(bufc)::value;
+    int id[NL];
+    const bool nx = t + 1 < nkt;
+    if (nx) ids_of(t + 1, id);
+    load_ids(t + 2);
+    if (nx) {
+      stage_rows<BN, D>(hk, id, B1 ? ks0 : ks1, wave, lane);
+      stage_rows<BN, D>(hv, id, B1 ? vs0 : vs1, wave, lane);
+    }
+    const int k0 = t * BN;
+    if ((causal && k0 + BN - 1 > qw) || k0 + BN > S)
+      plain_tile(std::true_type{}, t, bufc);
+    else
+      plain_tile(std::false_type{}, t, bufc);
+    wait_vmem();
+    __syncthreads();
+  };
+
+  if constexpr (PIPE) {
+    load_ids(0);
+    load_ids(1);
+    load_ids(2);
+    wait_vmem();
+    __syncthreads();
+    {
+      int id0[NL], id1[NL];
+      ids_of(0, id0);
+      if (nkt > 1) ids_of(1, id1);
+      stage_rows<BN, D>(hk, id0, ks0, wave, lane);
+      stage_rows<BN, D>(hv, id0, vs0, wave, lane);
+      if (nkt > 1) stage_rows<BN, D>(hk, id1, ks1, wave, lane);
+    }
+    wait_vmem();
+    __syncthreads();
+    f32x16 sa[2], sb[2];
+    scores(sa, std::false_type{});
+    __syncthreads();  // K(0)'s buffer is refilled by the first step
+    for (int t = 0; t < nkt; t += 2) {
+      step(t, sa, sb, std::false_type{});
+      if (t + 1 < nkt) step(t + 1, sb, sa, std::true_type{});
+    }
+  } else {
+    load_ids(0);
+    load_ids(1);
+    wait_vmem();
+    __syncthreads();
+    {
+      int id0[NL];
+      ids_of(0, id0);
+      stage_rows<BN, D>(hk, id0, ks0, wave, lane);
+      stage_rows<BN, D>(hv, id0, vs0, wave, lane);
+    }
+    wait_vmem();
+    __syncthreads();
+    for (int t = 0; t < nkt; t += 2) {
+      plain_step(t, std::false_type{});
+      if (t + 1 < nkt) plain_step(t + 1, std::true_type{});
+    }
+  }
+
+  const float l_own = l_run - l_cmp;
+  const float l_tot = pair_sum(l_own);
+  const float inv_l = 1.0f / l_tot;
+  if (myq < a.o_rows) {
+    float* orow = a.o + b * a.osb + h * a.osh + static_cast<int64_t>(myq) * a.oss;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 val = make_float4(oacc[db][4 * g] * inv_l, oacc[db][4 * g + 1] * inv_l,
+                                       oacc[db][4 * g + 2] * inv_l, oacc[db][4 * g + 3] * inv_l);
+        *reinterpret_cast<float4*>(orow + db * 32 + g * 8 + hl * 4) = val;
+      }
+  }
+  if (hl == 0) a.lse[bh * Sp + myq] = m_run + log2f(l_tot);  // base-2 log-sum-exp
+}
+
+// Two waves per SIMD: the pipelined loop at D = 64, the plain loop at D = 128 (the pipeline's
+// extra registers would force one wave there, which cannot hide its vector work).
+#define LH_FWD(NAME, D, PIPE, MAPPED)                                                        \
+  __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void NAME( \
+      FwdArgs a) {                                                                          \
+    attn_fwd_body<D, PIPE, MAPPED>(a);                                                      \
+  }
+LH_FWD(attn_fwd_d64, 64, true, false)
+LH_FWD(attn_fwd_d128, 128, false, false)
+LH_FWD(attn_fwd_mapped_d64, 64, true, true)
+LH_FWD(attn_fwd_mapped_d128, 128, false, true)
+#undef LH_FWD
+
+// ------------------------------------------------------------------------ backward
+struct BwdArgs {
+  RowSrc q, k, v;
+  const int32_t* gmap;        // mapped: [B*H, Sp]
+  const uint16_t* dout;       // dO rows at dout + b dsb + h dsh + s dss (bf16)
+  int64_t dsb, dsh, dss;
+  const float* lse;           // [B*H, Sp], base 2
+  const float* delta;         // [B*H, Sp] (zero for padding)
+  float* dq;                  // gradient rows at g + b gsb + h gsh + s gss
+  float* dk;
+  float* dv;
+  int64_t gsb, gsh, gss;
+  int64_t BH;
+  int H, S, Sp, g_rows, causal;
+  float scale, sl2;
+};
+
+// ---------------------------------------------------------------- key pass (dK, dV)
+// Workgroup = 128 keys (4 waves x 32); loops over query tiles of BQ from the diagonal down.
+// S = Q K^T and dP = dO V^T with keys as the C column, so P and dS leave the C registers as
+// B operands of dV^T = dO^T P and dK^T = Q^T dS, whose A operands are transposing reads of
+// the staged dO and Q row tiles.  V is negated once and the dP accumulator is seeded with
+// Delta, so the product yields Delta - dP and dS costs one multiply (the sign is folded into
+// the final dK scale).
+template <int D, int BQ, bool MAPPED>
+__device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
+  constexpr int BK = 128, NB = BQ / 32;
+  using QT = Tile<BQ, D>;
+  constexpr int NL = QT::LOADS;
+  // each buffer its own LDS object, named statically (the loop is unrolled by two): the
+  // compiler then does not make a tile's LDS reads wait for the next tile's loads
+  __shared__ __attribute__((aligned(16))) uint16_t qs0[BQ * D], qs1[BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t ds0[BQ * D], ds1[BQ * D];
+  __shared__ __attribute__((aligned(16))) float ls0[BQ], ls1[BQ];
+  __shared__ __attribute__((aligned(16))) float dl0[BQ], dl1[BQ];
+  __shared__ __attribute__((aligned(16))) int32_t idr[4][BQ];
+
+  const int S = a.S, Sp = a.Sp;
+  const int nkt = Sp / BK;
+  const int64_t item = xcd_item(blockIdx.x, a.BH * nkt);
+  const int64_t bh = item / nkt;
+  const int ktile = static_cast<int>(item % nkt);  // small key tiles have the most work: first
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, lq = lane & 31;
+  const int K0 = ktile * BK;
+  const int kw = K0 + wave * 32;
+  const int mykey = kw + lq;
+  const bool causal = a.causal != 0;
+  const HeadRows hq = head_rows(a.q, b, h), hk = head_rows(a.k, b, h), hv = head_rows(a.v, b, h);
+  const int32_t* gm = MAPPED ? a.gmap + bh * Sp : nullptr;
+  const uint16_t* dob = a.dout + b * a.dsb + h * a.dsh;
+  const float* lb = a.lse + bh * Sp;
+  const float* dlb = a.delta + bh * Sp;
+  const float sl2 = a.sl2;
+
+  bf16x8 kreg[D / 16], vreg[D / 16];
+  {
+    const int kid = MAPPED ? max(gm[mykey], 0) : min(mykey, S - 1);
+    const uint16_t* kr = row_ptr(hk, kid);
+    const uint16_t* vr = row_ptr(hv, kid);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      kreg[kk] = ld_op16(kr + 16 * kk + hl * 8);
+      // -V: the dP product then accumulates Delta - dP on top of Delta
+      vreg[kk] = as_bf16x8(__builtin_bit_cast(u32x4, ld_op16(vr + 16 * kk + hl * 8)) ^ 0x80008000u);
+    }
+  }
+  f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+  for (int d2 = 0; d2 < D / 32; ++d2) {
+    dkacc[d2] = zero16();
+    dvacc[d2] = zero16();
+  }
+
+  const int qt0 = causal ? K0 / BQ : 0;
+  const int nqt = (S + BQ - 1) / BQ;
+
+  auto load_ids = [&](int t) {
+    if constexpr (MAPPED)
+      if (wave == 0 && t < nqt) stage_words(gm + t * BQ, idr[t & 3], lane, BQ);
+  };
+  // Tile t: Q rows (through the map), dO rows, lse and Delta into buffer B1; the ids are read
+  // from LDS before any load of this step is issued.
+  auto stage = [&](int t, auto bufc) {
+    constexpr bool B1 = decltype(bufc)::value;
+    const int q0 = t * BQ;
+    int id[NL], ido[NL];
+    tile_ids<BQ, D, MAPPED>(idr[t & 3], q0, S, wave, lane, id);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) ido[i] = min(q0 + QT::row(i, wave, lane), S - 1);
+    load_ids(t + 1);
+    stage_rows<BQ, D>(hq, id, B1 ? qs1 : qs0, wave, lane);
+    HeadRows hd;
+    hd.x = dob;
+    hd.p = nullptr;
+    hd.ss = a.dss;
+    hd.n0 = int64_t(1) << 62;
+    stage_rows<BQ, D>(hd, ido, B1 ? ds1 : ds0, wave, lane);
+    if (wave == 0) stage_words(lb + q0, B1 ? ls1 : ls0, lane, BQ);
+    if (wave == 1) stage_words(dlb + q0, B1 ? dl1 : dl0, lane, BQ);
+  };
+
+  // generic tile (any D, BQ): S and dP per 32-query block, then dV and dK per 16-query chunk
+  auto tile = [&](auto masked, int t, auto bufc) {
+    constexpr bool B1 = decltype(bufc)::value;
+    const uint16_t* qsb = B1 ? qs1 : qs0;
+    const uint16_t* dsb = B1 ? ds1 : ds0;
+    const float* lsb = B1 ? ls1 : ls0;
+    const float* dlb_ = B1 ? dl1 : dl0;
+    const int q0 = t * BQ;
+    f32x16 sacc[NB], pacc[NB];
+#pragma unroll
+    for (int b2 = 0; b2 < NB; ++b2) {
+      sacc[b2] = zero16();
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 d4 = *reinterpret_cast<const float4*>(&dlb_[b2 * 32 + g * 8 + hl * 4]);
+        pacc[b2][4 * g] = d4.x;
+        pacc[b2][4 * g + 1] = d4.y;
+        pacc[b2][4 * g + 2] = d4.z;
+        pacc[b2][4 * g + 3] = d4.w;
+      }
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        sacc[b2] = mfma32(lds_at(qsb, b2 * 64 * D + op_off<D>(lq, hl, kk)), kreg[kk], sacc[b2]);
+        pacc[b2] = mfma32(lds_at(dsb, b2 * 64 * D + op_off<D>(lq, hl, kk)), vreg[kk], pacc[b2]);
+      }
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < NB; ++b2)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qi = b2 * 32 + g * 8 + hl * 4;
+        const float4 l4 = *reinterpret_cast<const float4*>(&lsb[qi]);
+        const float lv4[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = g * 4 + u;
+          float p = __builtin_amdgcn_exp2f(fmaf(sacc[b2][r], sl2, -lv4[u]));
+          if constexpr (decltype(masked)::value) {
+            const int qa = q0 + qi + u;
+            if ((causal && qa < mykey) || qa >= S) p = 0.f;
+          }
+          sacc[b2][r] = p;
+          pacc[b2][r] = p * pacc[b2][r];
+        }
+      }
+#pragma unroll
+    for (int t4 = 0; t4 < 2 * NB; ++t4) {
+      bf16x8 ph, pl, sh, sl;
+      c_to_op2(sacc[t4 >> 1], t4 & 1, ph, pl);
+      c_to_op2(pacc[t4 >> 1], t4 & 1, sh, sl);
+#pragma unroll
+      for (int d2 = 0; d2 < D / 32; ++d2) {
+        // transposing-read offsets, computed per use to keep registers free
+        const uint32_t o0 = t4 * 32 * D + tr_off<D>(lane, d2, 0);
+        const uint32_t o1 = t4 * 32 * D + tr_off<D>(lane, d2, 1);
+        const bf16x8 ao = tr_op(dsb, o0, o1);
+        const bf16x8 aq = tr_op(qsb, o0, o1);
+        dvacc[d2] = mfma32(ao, pl, dvacc[d2]);
+        dvacc[d2] = mfma32(ao, ph, dvacc[d2]);
+        dkacc[d2] = mfma32(aq, sl, dkacc[d2]);
+        dkacc[d2] = mfma32(aq, sh, dkacc[d2]);
+      }
+    }
+  };
+
+  // D = 64, 64 queries: twelve groups of four MFMAs (A: S and dP of one 32-query block, two k
+  // steps; V / K: the dV or dK update of one 16-query chunk), each carrying vector work whose
+  // inputs are complete:
+  //   A00 -          A01 -            A10 b0 b1     A11 p0 d0     V0 p1   K0 d1
+  //   V1 b2 b3       K1 p2 d2         V2 p3         K2 d3         V3 -    K3 -
+  // (b = exp and dS of chunk t4, p / d = hi-lo split of P / dS of chunk t4), fixed with
+  // scheduling barriers; the LDS operands of each group are read one group ahead.
+  uint32_t loff[4], tro[2][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) loff[j] = op_off<64>(lq, hl, j);
+#pragma unroll
+  for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) tro[d2][sec] = tr_off<64>(lane, d2, sec);
+
+  auto tile64 = [&](auto masked, int t, auto bufc) {
+    constexpr bool MASK = decltype(masked)::value;
+    constexpr bool B1 = decltype(bufc)::value;
+    const int q0 = t * BQ;
+    const uint16_t* qsb = B1 ? qs1 : qs0;
+    const uint16_t* dsb = B1 ? ds1 : ds0;
+    const float* lsb = B1 ? ls1 : ls0;
+    const float* dlb_ = B1 ? dl1 : dl0;
+    f32x16 sacc[2], pacc[2];
+    bf16x8 op[12][4];
+    float4 lsv[2][4];
+    bf16x8 ph[4], pl[4], sh[4], sl[4];
+    // opaque copies: the address sums stay inside the loop and fold into instruction
+    // offsets instead of being hoisted into dozens of live registers
+    uint32_t lo[4], tr[2][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[j] = loff[j];
+      asm volatile("" : "+v"(lo[j]));
+    }
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        tr[d2][sec] = tro[d2][sec];
+        asm volatile("" : "+v"(tr[d2][sec]));
+      }
+    auto rd = [&](const uint16_t* tile_base, int m, int j) {
+      return lds_at(tile_base, 4096 * m + lo[j]);
+    };
+    auto load_ops = [&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u < 4) {
+        constexpr int b2 = u >> 1, kh = u & 1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int kk = 2 * kh + j;
+          op[u][2 * j] = rd(qsb, b2, kk);
+          op[u][2 * j + 1] = rd(dsb, b2, kk);
+        }
+      } else {
+        constexpr int c = u - 4, t4 = c >> 1;
+        const uint16_t* src = (c & 1) ? qsb : dsb;
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2)
+          op[u][d2] = tr_op(src, 2048 * t4 + tr[d2][0], 2048 * t4 + tr[d2][1]);
+      }
+    };
+    auto mfma_unit = [&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u < 4) {
+        constexpr int b2 = u >> 1, kh = u & 1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int kk = 2 * kh + j;
+          sacc[b2] = mfma32(op[u][2 * j], kreg[kk], sacc[b2]);
+          pacc[b2] = mfma32(op[u][2 * j + 1], vreg[kk], pacc[b2]);
+        }
+      } else if constexpr (((u - 4) & 1) == 0) {
+        constexpr int t4 = (u - 4) >> 1;
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) dvacc[d2] = mfma32(op[u][d2], pl[t4], dvacc[d2]);
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) dvacc[d2] = mfma32(op[u][d2], ph[t4], dvacc[d2]);
+      } else {
+        constexpr int t4 = (u - 4) >> 1;
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) dkacc[d2] = mfma32(op[u][d2], sl[t4], dkacc[d2]);
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) dkacc[d2] = mfma32(op[u][d2], sh[t4], dkacc[d2]);
+      }
+    };
+    auto load_ls = [&](int b2) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        lsv[b2][g] = *reinterpret_cast<const float4*>(&lsb[b2 * 32 + g * 8 + hl * 4]);
+    };
+    auto b_unit = [&](int t4) {
+      const int b2 = t4 >> 1, half = t4 & 1;
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int g = 2 * half + gg;
+        const float lv4[4] = {lsv[b2][g].x, lsv[b2][g].y, lsv[b2][g].z, lsv[b2][g].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = g * 4 + u;
+          float p = __builtin_amdgcn_exp2f(fmaf(sacc[b2][r], sl2, -lv4[u]));
+          if constexpr (MASK) {
+            const int qa = q0 + b2 * 32 + g * 8 + hl * 4 + u;
+            if ((causal && qa < mykey) || qa >= S) p = 0.f;
+          }
+          sacc[b2][r] = p;
+          pacc[b2][r] = p * pacc[b2][r];
+        }
+      }
+    };
+    auto sp_unit = [&](int t4) { c_to_op2(sacc[t4 >> 1], t4 & 1, ph[t4], pl[t4]); };
+    auto sd_unit = [&](int t4) { c_to_op2(pacc[t4 >> 1], t4 & 1, sh[t4], sl[t4]); };
+    auto layout = [&](auto nvc) {
+      constexpr int nv = decltype(nvc)::value;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using N0 = std::integral_constant<int, 0>;
+    using N6 = std::integral_constant<int, 6>;
+    using N12 = std::integral_constant<int, 12>;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    using I6 = std::integral_constant<int, 6>;
+    using I7 = std::integral_constant<int, 7>;
+    using I8 = std::integral_constant<int, 8>;
+    using I9 = std::integral_constant<int, 9>;
+    using I10 = std::integral_constant<int, 10>;
+    using I11 = std::integral_constant<int, 11>;
+    auto seed = [&](int b2) {
+      sacc[b2] = zero16();
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 d4 = *reinterpret_cast<const float4*>(&dlb_[b2 * 32 + g * 8 + hl * 4]);
+        pacc[b2][4 * g] = d4.x;
+        pacc[b2][4 * g + 1] = d4.y;
+        pacc[b2][4 * g + 2] = d4.z;
+        pacc[b2][4 * g + 3] = d4.w;
+      }
+    };
+    seed(0);
+    load_ops(I0{});
+    __builtin_amdgcn_sched_barrier(0);
+    load_ops(I1{});
+    mfma_unit(I0{});
+    layout(N0{});
+    load_ops(I2{});
+    seed(1);
+    load_ls(0);
+    mfma_unit(I1{});
+    layout(N0{});
+    load_ops(I3{});
+    mfma_unit(I2{});
+    b_unit(0);
+    b_unit(1);
+    layout(N12{});
+    load_ops(I4{});
+    mfma_unit(I3{});
+    sp_unit(0);
+    sd_unit(0);
+    layout(N12{});
+    load_ops(I5{});
+    load_ls(1);
+    mfma_unit(I4{});
+    sp_unit(1);
+    layout(N6{});
+    load_ops(I6{});
+    mfma_unit(I5{});
+    sd_unit(1);
+    layout(N6{});
+    load_ops(I7{});
+    mfma_unit(I6{});
+    b_unit(2);
+    b_unit(3);
+    layout(N12{});
+    load_ops(I8{});
+    mfma_unit(I7{});
+    sp_unit(2);
+    sd_unit(2);
+    layout(N12{});
+    load_ops(I9{});
+    mfma_unit(I8{});
+    sp_unit(3);
+    layout(N6{});
+    load_ops(I10{});
+    mfma_unit(I9{});
+    sd_unit(3);
+    layout(N6{});
+    load_ops(I11{});
+    mfma_unit(I10{});
+    layout(N0{});
+    mfma_unit(I11{});
+    layout(N0{});
+  };
+
+  auto step = [&](int t, auto bufc) {
+    if (t + 1 < nqt) stage(t + 1, std::integral_constant<bool, !decltype(bufc)::value>{});
+    const int q0 = t * BQ;
+    const bool msk = (causal && q0 < kw + 31) || q0 + BQ > S;
+    if constexpr (D == 64 && BQ == 64) {
+      if (msk)
+        tile64(std::true_type{}, t, bufc);
+      else
+        tile64(std::false_type{}, t, bufc);
+    } else {
+      if (msk)
+        tile(std::true_type{}, t, bufc);
+      else
+        tile(std::false_type{}, t, bufc);
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+  if (qt0 < nqt) {
+    load_ids(qt0);
+    wait_vmem();
+    __syncthreads();
+    stage(qt0, std::false_type{});
+  }
+  wait_vmem();
+  __syncthreads();
+  for (int t = qt0; t < nqt; t += 2) {
+    step(t, std::false_type{});
+    if (t + 1 < nqt) step(t + 1, std::true_type{});
+  }
+
+  if (mykey < a.g_rows) {
+    float* dkr = a.dk + b * a.gsb + h * a.gsh + static_cast<int64_t>(mykey) * a.gss;
+    float* dvr = a.dv + b * a.gsb + h * a.gsh + static_cast<int64_t>(mykey) * a.gss;
+    const bool live = mykey < S;
+#pragma unroll
+    for (int d2 = 0; d2 < D / 32; ++d2)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float ns = -a.scale;  // dkacc holds -dS^T Q
+        float4 x = make_float4(dkacc[d2][4 * g] * ns, dkacc[d2][4 * g + 1] * ns,
+                               dkacc[d2][4 * g + 2] * ns, dkacc[d2][4 * g + 3] * ns);
+        float4 y = make_float4(dvacc[d2][4 * g], dvacc[d2][4 * g + 1], dvacc[d2][4 * g + 2],
+                               dvacc[d2][4 * g + 3]);
+        if (!live) x = y = make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(dkr + d2 * 32 + g * 8 + hl * 4) = x;
+        *reinterpret_cast<float4*>(dvr + d2 * 32 + g * 8 + hl * 4) = y;
+      }
+  }
+}
+
+// -------------------------------------------------------------- query pass (dQ)
+// Workgroup = 128 queries (the forward's layout) over key tiles of BN: S^T = K Q^T and
+// dP^T = V dO^T (K and V rows staged), dS^T feeds dQ^T = K^T dS^T as the B operand, with K^T
+// read from the staged K rows by transposing reads.
+template <int D, int BN, bool MAPPED>
+__device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
+  constexpr int BM = 128, NBK = BN / 32;
+  using KT = Tile<BN, D>;
+  constexpr int NL = KT::LOADS;
+  __shared__ __attribute__((aligned(16))) uint16_t ks0[BN * D], ks1[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs0[BN * D], vs1[BN * D];
+  __shared__ __attribute__((aligned(16))) int32_t idr[4][BN];
+
+  const int S = a.S, Sp = a.Sp;
+  const int nqt = Sp / BM;
+  const int64_t item = xcd_item(blockIdx.x, a.BH * nqt);
+  const int64_t bh = item / nqt;
+  const int qtile = nqt - 1 - static_cast<int>(item % nqt);
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, lq = lane & 31;
+  const int Q0 = qtile * BM;
+  const int qw = Q0 + wave * 32;
+  const int myq = qw + lq;
+  const bool causal = a.causal != 0;
+  const HeadRows hq = head_rows(a.q, b, h), hk = head_rows(a.k, b, h), hv = head_rows(a.v, b, h);
+  const int32_t* gm = MAPPED ? a.gmap + bh * Sp : nullptr;
+  const float sl2 = a.sl2;
+
+  bf16x8 qreg[D / 16], oreg[D / 16];
+  {
+    const int qid = MAPPED ? max(gm[myq], 0) : min(myq, S - 1);
+    const uint16_t* qr = row_ptr(hq, qid);
+    const uint16_t* dr = a.dout + b * a.dsb + h * a.dsh + static_cast<int64_t>(min(myq, S - 1)) * a.dss;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      qreg[kk] = ld_op16(qr + 16 * kk + hl * 8);
+      oreg[kk] = ld_op16(dr + 16 * kk + hl * 8);
+    }
+  }
+  const float l2 = a.lse[bh * Sp + myq];
+  const float dlt = a.delta[bh * Sp + myq];
+
+  f32x16 dqacc[D / 32];
+#pragma unroll
+  for (int d2 = 0; d2 < D / 32; ++d2) dqacc[d2] = zero16();
+
+  const int kend = causal ? (S < Q0 + BM ? S : Q0 + BM) : S;
+  const int nkt = (kend + BN - 1) / BN;
+  uint32_t koff[D / 16];
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) koff[j] = op_off<D>(lq, hl, j);
+
+  auto load_ids = [&](int t) {
+    if constexpr (MAPPED)
+      if (wave == 0 && t < nkt) stage_words(gm + t * BN, idr[t & 3], lane, BN);
+  };
+  auto stage = [&](int t, auto bufc) {
+    constexpr bool B1 = decltype(bufc)::value;
+    int id[NL];
+    tile_ids<BN, D, MAPPED>(idr[t & 3], t * BN, S, wave, lane, id);
+    load_ids(t + 1);
+    stage_rows<BN, D>(hk, id, B1 ? ks1 : ks0, wave, lane);
+    stage_rows<BN, D>(hv, id, B1 ? vs1 : vs0, wave, lane);
+  };
+
+  auto tile = [&](auto masked, int t, auto bufc) {
+    constexpr bool B1 = decltype(bufc)::value;
+    const uint16_t* ksb = B1 ? ks1 : ks0;
+    const uint16_t* vsb = B1 ? vs1 : vs0;
+    const int k0 = t * BN;
+    uint32_t ko[D / 16];
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      ko[j] = koff[j];
+      asm volatile("" : "+v"(ko[j]));
+    }
+    f32x16 sacc[NBK], pacc[NBK];
+#pragma unroll
+    for (int b2 = 0; b2 < NBK; ++b2) {
+      sacc[b2] = zero16();
+      pacc[b2] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        sacc[b2] = mfma32(lds_at(ksb, b2 * 64 * D + ko[kk]), qreg[kk], sacc[b2]);
+        pacc[b2] = mfma32(lds_at(vsb, b2 * 64 * D + ko[kk]), oreg[kk], pacc[b2]);
+      }
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < NBK; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(sacc[b2][r], sl2, -l2));
+        if constexpr (decltype(masked)::value) {
+          const int key = k0 + b2 * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+          if ((causal && key > myq) || key >= S) p = 0.f;
+        }
+        pacc[b2][r] = p * (pacc[b2][r] - dlt);
+      }
+#pragma unroll
+    for (int t4 = 0; t4 < 2 * NBK; ++t4) {
+      bf16x8 sh, sl;
+      c_to_op2(pacc[t4 >> 1], t4 & 1, sh, sl);
+#pragma unroll
+      for (int d2 = 0; d2 < D / 32; ++d2) {
+        const uint32_t o0 = t4 * 32 * D + tr_off<D>(lane, d2, 0);
+        const uint32_t o1 = t4 * 32 * D + tr_off<D>(lane, d2, 1);
+        const bf16x8 ak = tr_op(ksb, o0, o1);
+        dqacc[d2] = mfma32(ak, sl, dqacc[d2]);
+        dqacc[d2] = mfma32(ak, sh, dqacc[d2]);
+      }
+    }
+  };
+
+  auto step = [&](int t, auto bufc) {
+    if (t + 1 < nkt) stage(t + 1, std::integral_constant<bool, !decltype(bufc)::value>{});
+    const int k0 = t * BN;
+    if ((causal && k0 + BN - 1 > qw) || k0 + BN > S)
+      tile(std::true_type{}, t, bufc);
+    else
+      tile(std::false_type{}, t, bufc);
+    wait_vmem();
+    __syncthreads();
+  };
+  load_ids(0);
+  wait_vmem();
+  __syncthreads();
+  stage(0, std::false_type{});
+  wait_vmem();
+  __syncthreads();
+  for (int t = 0; t < nkt; t += 2) {
+    step(t, std::false_type{});
+    if (t + 1 < nkt) step(t + 1, std::true_type{});
+  }
+
+  if (myq < a.g_rows) {
+    float* dqr = a.dq + b * a.gsb + h * a.gsh + static_cast<int64_t>(myq) * a.gss;
+    const bool live = myq < S;
+#pragma unroll
+    for (int d2 = 0; d2 < D / 32; ++d2)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4 x = make_float4(dqacc[d2][4 * g] * a.scale, dqacc[d2][4 * g + 1] * a.scale,
+                               dqacc[d2][4 * g + 2] * a.scale, dqacc[d2][4 * g + 3] * a.scale);
+        if (!live) x = make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(dqr + d2 * 32 + g * 8 + hl * 4) = x;
+      }
+  }
+}
+
+// Occupancy: at D = 64 both passes run two waves per SIMD; at D = 128 the query pass runs two
+// waves with 32-key tiles, the key pass one wave (its accumulators live in AGPRs).
+#define LH_KV(NAME, D, BQ, MAPPED, ATTR)                                  \
+  __global__ __launch_bounds__(256) ATTR void NAME(BwdArgs a) {           \
+    attn_bwd_kv_body<D, BQ, MAPPED>(a);                                   \
+  }
+#define LH_Q(NAME, D, BN, MAPPED)                                                          \
+  __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void NAME( \
+      BwdArgs a) {                                                                         \
+    attn_bwd_q_body<D, BN, MAPPED>(a);                                                     \
+  }
+#define LH_TWO_WAVES __attribute__((amdgpu_waves_per_eu(2, 2)))
+#define LH_ONE_WAVE
+LH_KV(attn_bwd_kv_d64, 64, 64, false, LH_TWO_WAVES)
+LH_KV(attn_bwd_kv_d128, 128, 32, false, LH_ONE_WAVE)
+LH_KV(attn_bwd_kv_mapped_d64, 64, 64, true, LH_TWO_WAVES)
+LH_KV(attn_bwd_kv_mapped_d128, 128, 32, true, LH_ONE_WAVE)
+LH_Q(attn_bwd_q_d64, 64, 64, false)
+LH_Q(attn_bwd_q_d128, 128, 32, false)
+LH_Q(attn_bwd_q_mapped_d64, 64, 64, true)
+LH_Q(attn_bwd_q_mapped_d128, 128, 32, true)
+#undef LH_KV
+#undef LH_Q
+#undef LH_TWO_WAVES
+#undef LH_ONE_WAVE
+
+// Delta[b, h, s] = sum_d dO[s, d] O[s, d] for s < S, 0 for the padding up to Sp: one wave per
+// row group, D / 8 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ dout, int64_t dsb,
+                                                   int64_t dsh, int64_t dss,
+                                                   const float* __restrict__ o, int64_t osb,
+                                                   int64_t osh, int64_t oss,
+                                                   float* __restrict__ delta, int64_t BH, int H,
+                                                   int S, int Sp) {
+  constexpr int G = D / 8;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t row = gid / G;
+  const int g = static_cast<int>(gid % G);
+  if (row >= BH * Sp) return;
+  const int64_t bh = row / Sp;
+  const int s = static_cast<int>(row % Sp);
+  const int64_t b = bh / H, h = bh % H;
+  float part = 0.f;
+  if (s < S) {
+    const uint4 u = *reinterpret_cast<const uint4*>(dout + b * dsb + h * dsh + s * dss + g * 8);
+    const float* orow = o + b * osb + h * osh + s * oss + g * 8;
+    const float4 o0 = *reinterpret_cast<const float4*>(orow);
+    const float4 o1 = *reinterpret_cast<const float4*>(orow + 4);
+    const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      part = fmaf(__uint_as_float(w[i] << 16), ov[2 * i], part);
+      part = fmaf(__uint_as_float(w[i] & 0xffff0000u), ov[2 * i + 1], part);
+    }
+  }
+  for (int m = 1; m < G; m <<= 1) part += __shfl_xor(part, m);
+  if (g == 0) delta[bh * Sp + s] = part;
+}
+
+RowSrc strided_rows(const void* x, const int64_t st[3]) {
+  RowSrc r;
+  r.x = static_cast<const uint16_t*>(x);
+  r.px = nullptr;
+  r.sb = st[0];
+  r.sh = st[1];
+  r.ss = st[2];
+  r.psb = 0;
+  r.n0 = int64_t(1) << 62;
+  return r;
+}
+
+// Rows of a [B, N, H, D] token tensor and its pooled levels [B, P1, H, D] addressed by
+// pyramid id.
+RowSrc mapped_rows(const Levels& lv, const void* x, const void* px) {
+  RowSrc r;
+  r.x = static_cast<const uint16_t*>(x);
+  r.px = static_cast<const uint16_t*>(px);
+  r.sb = lv.N * lv.H * lv.D;
+  r.sh = lv.D;
+  r.ss = static_cast<int64_t>(lv.H) * lv.D;
+  r.psb = lv.P1 * lv.H * lv.D;
+  r.n0 = lv.N;
+  return r;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------ launchers
+hipError_t launch_attn_fwd2(const AttnCall& c, const void* q, const void* k, const void* v,
+                            float* o, float* lse, hipStream_t st) {
+  FwdArgs a;
+  if (c.mapped) {
+    a.q = mapped_rows(*c.lv, q, c.pq);
+    a.k = mapped_rows(*c.lv, k, c.pk);
+    a.v = mapped_rows(*c.lv, v, c.pv);
+  } else {
+    a.q = strided_rows(q, c.q_stride);
+    a.k = strided_rows(k, c.k_stride);
+    a.v = strided_rows(v, c.v_stride);
+  }
+  a.gmap = c.gmap;
+  a.o = o;
+  a.osb = c.o_stride[0];
+  a.osh = c.o_stride[1];
+  a.oss = c.o_stride[2];
+  a.lse = lse;
+  a.BH = c.B * c.H;
+  a.H = static_cast<int>(c.H);
+  a.S = static_cast<int>(c.S);
+  a.Sp = static_cast<int>(padded_len(c.S));
+  a.o_rows = c.o_rows;
+  a.causal = c.causal;
+  a.sl2 = c.scale * kLog2e;
+  const unsigned blocks = static_cast<unsigned>(a.BH * (a.Sp / 128));
+  if (c.D == 64)
+    hipLaunchKernelGGL(c.mapped ? attn_fwd_mapped_d64 : attn_fwd_d64, dim3(blocks), dim3(256), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL(c.mapped ? attn_fwd_mapped_d128 : attn_fwd_d128, dim3(blocks), dim3(256),
+                       0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd2(int pass, const AttnCall& c, const void* q, const void* k,
+                            const void* v, const void* dout, const float* lse,
+                            const float* delta, float* dq, float* dk, float* dv, hipStream_t st) {
+  BwdArgs a;
+  if (c.mapped) {
+    a.q = mapped_rows(*c.lv, q, c.pq);
+    a.k = mapped_rows(*c.lv, k, c.pk);
+    a.v = mapped_rows(*c.lv, v, c.pv);
+  } else {
+    a.q = strided_rows(q, c.q_stride);
+    a.k = strided_rows(k, c.k_stride);
+    a.v = strided_rows(v, c.v_stride);
+  }
+  a.gmap = c.gmap;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dsb = c.do_stride[0];
+  a.dsh = c.do_stride[1];
+  a.dss = c.do_stride[2];
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.gsb = c.g_stride[0];
+  a.gsh = c.g_stride[1];
+  a.gss = c.g_stride[2];
+  a.BH = c.B * c.H;
+  a.H = static_cast<int>(c.H);
+  a.S = static_cast<int>(c.S);
+  a.Sp = static_cast<int>(padded_len(c.S));
+  a.g_rows = c.o_rows;
+  a.causal = c.causal;
+  a.scale = c.scale;
+  a.sl2 = c.scale * kLog2e;
+  const unsigned blocks = static_cast<unsigned>(a.BH * (a.Sp / 128));
+  if (pass & 1) {
+    if (c.D == 64)
+      hipLaunchKernelGGL(c.mapped ? attn_bwd_kv_mapped_d64 : attn_bwd_kv_d64, dim3(blocks),
+                         dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(c.mapped ? attn_bwd_kv_mapped_d128 : attn_bwd_kv_d128, dim3(blocks),
+                         dim3(256), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (pass & 2) {
+    if (c.D == 64)
+      hipLaunchKernelGGL(c.mapped ? attn_bwd_q_mapped_d64 : attn_bwd_q_d64, dim3(blocks),
+                         dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(c.mapped ? attn_bwd_q_mapped_d128 : attn_bwd_q_d128, dim3(blocks),
+                         dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_delta(const AttnCall& c, const void* dout, const float* o, float* delta,
+                             hipStream_t st) {
+  const int64_t BH = c.B * c.H, Sp = padded_len(c.S);
+  const int64_t threads = BH * Sp * (c.D / 8);
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  const auto* d = static_cast<const uint16_t*>(dout);
+  if (c.D == 64)
+    hipLaunchKernelGGL(delta_kernel<64>, grid, dim3(256), 0, st, d, c.do_stride[0],
+                       c.do_stride[1], c.do_stride[2], o, c.o_stride[0], c.o_stride[1],
+                       c.o_stride[2], delta, BH, static_cast<int>(c.H), static_cast<int>(c.S),
+                       static_cast<int>(Sp));
+  else
+    hipLaunchKernelGGL(delta_kernel<128>, grid, dim3(256), 0, st, d, c.do_stride[0],
+                       c.do_stride[1], c.do_stride[2], o, c.o_stride[0], c.o_stride[1],
+                       c.o_stride[2], delta, BH, static_cast<int>(c.H), static_cast<int>(c.S),
+                       static_cast<int>(Sp));
+  return hipGetLastError();
+}
+
+}  // namespace lh

@@ -61,6 +61,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // 128 (one forward query tile); padding rows are written as finite values (zeros).
 inline int64_t padded_len(int64_t S) { return (S + 127) / 128 * 128; }
 
+// One attention call: shapes, where the rows of Q, K, V live, and where results go.
+// Strides are in elements for (batch, head, sequence position).  Mapped calls read row s of
+// head (b, h) as pyramid entry gmap[b, h, s] of the token tensors q/k/v ([B, N, H, D]) or of
+// the pooled levels pq/pk/pv ([B, P1, H, D]); the q/k/v strides are then unused.
+struct AttnCall {
+  int64_t B, H, S;
+  int32_t D;
+  float scale;
+  int32_t causal;
+  int32_t o_rows;  // rows per head written to O and to the gradients (S, or Sp when padded)
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3], do_stride[3], g_stride[3];
+  int32_t mapped;
+  const Levels* lv;
+  const int32_t* gmap;  // [B*H, Sp]
+  const void* pq;
+  const void* pk;
+  const void* pv;
+};
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already validated.
 hipError_t launch_pool_score(const Levels& lv, int32_t in_f32, const void* q, const void* k,
@@ -69,28 +88,28 @@ hipError_t launch_pool_score(const Levels& lv, int32_t in_f32, const void* q, co
 hipError_t launch_topk(const Levels& lv, const float* scores, int32_t* sel, hipStream_t st);
 hipError_t launch_build_map(const Levels& lv, const int32_t* sel, int32_t* gmap, int32_t* inv,
                             hipStream_t st);
+// Gathered rows [B, H, Sp, D] bf16 of q/k/v (level 0) or the pooled levels (gmap ids).
 hipError_t launch_gather(const Levels& lv, int32_t in_f32, const void* x[3], const void* px[3],
                          int32_t pooled_f32, const int32_t* gmap, void* const rows[3],
-                         void* const trans[3], hipStream_t st);
-hipError_t launch_attn_fwd(int64_t B, int64_t H, int64_t S, int32_t D, float scale,
-                           const void* q, const void* k, const void* vt, float* o, float* lse,
-                           hipStream_t st);
-hipError_t launch_attn_bwd(int64_t B, int64_t H, int64_t S, int32_t D, float scale,
-                           const void* q, const void* k, const void* v, const void* qt,
-                           const void* kt, const float* lse, const float* delta,
-                           const void* dout, const void* doutt, float* dq, float* dk,
-                           float* dv, hipStream_t st);
-// pass: 1 = key pass only, 2 = query pass only, 3 = both
-hipError_t launch_attn_bwd_pass(int pass, int64_t B, int64_t H, int64_t S, int32_t D,
-                                float scale, const void* q, const void* k, const void* v,
-                                const void* qt, const void* kt, const float* lse,
-                                const float* delta, const void* dout, const void* doutt,
-                                float* dq, float* dk, float* dv, hipStream_t st);
+                         hipStream_t st);
+// float32 -> bf16 (round to nearest even), n elements (n a multiple of 8).
+hipError_t launch_to_bf16(const float* x, void* y, int64_t n, hipStream_t st);
+// Attention over strided or mapped rows (lh_attn.hip).  lse / delta are [B*H, Sp].
+hipError_t launch_attn_fwd2(const AttnCall& c, const void* q, const void* k, const void* v,
+                            float* o, float* lse, hipStream_t st);
+// pass: 1 = key pass (dk, dv), 2 = query pass (dq), 3 = both; dout rows at c.do_stride,
+// gradients at c.g_stride.
+hipError_t launch_attn_bwd2(int pass, const AttnCall& c, const void* q, const void* k,
+                            const void* v, const void* dout, const float* lse,
+                            const float* delta, float* dq, float* dk, float* dv, hipStream_t st);
+// delta[b, h, s] = sum_d dout * o for s < S (rows at c.do_stride / c.o_stride), 0 up to Sp.
+hipError_t launch_attn_delta(const AttnCall& c, const void* dout, const float* o, float* delta,
+                             hipStream_t st);
 hipError_t launch_scatter(const Levels& lv, int32_t out_f32, const int32_t* inv,
                           const float* og, void* y, hipStream_t st);
 hipError_t launch_scatter_bwd(const Levels& lv, int32_t in_f32, const int32_t* gmap,
-                              const float* og, const void* dy, void* dog, void* dogt,
-                              float* delta, hipStream_t st);
+                              const float* og, const void* dy, void* dog, float* delta,
+                              hipStream_t st);
 hipError_t launch_gather_pool_bwd(const Levels& lv, int32_t out_f32, const int32_t* inv,
                                   const float* dqg, const float* dkg, const float* dvg,
                                   void* dq, void* dk, void* dv, hipStream_t st);

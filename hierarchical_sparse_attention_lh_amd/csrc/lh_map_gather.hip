@@ -19,12 +19,10 @@
 // that level's entries complete before the position -- one binary search in the kept list.
 // One thread per gathered entry; no atomics, no sort, and the result is the unique order.
 //
-// Gather design: one workgroup per 64 slots of one head.  Rows are copied with 16-byte
-// vectors into the row layout and staged in LDS to write the transposed layout with
-// 16-byte stores as well; the transposed layout stores slot s at column swap23(s), the
-// order in which the attention kernels consume it.  Padding slots S..Sp-1 are zeros.
+// Gather design (lh_gather only: the layer's own attention reads the rows through gmap and
+// never needs the copy): one workgroup per 64 slots of one head, rows copied with 16-byte
+// vectors, rounded to bf16; padding slots S..Sp-1 are zeros.
 #include "lh_internal.h"
-#include "lh_mfma.h"
 
 namespace lh {
 namespace {
@@ -141,12 +139,10 @@ __global__ __launch_bounds__(256) void gather_kernel(
     Levels lv, int64_t Sp, const Tin* __restrict__ x0, const Tin* __restrict__ x1,
     const Tin* __restrict__ x2, const Tpool* __restrict__ p0, const Tpool* __restrict__ p1,
     const Tpool* __restrict__ p2, const int32_t* __restrict__ gmap, uint16_t* r0, uint16_t* r1,
-    uint16_t* r2, uint16_t* t0, uint16_t* t1, uint16_t* t2) {
+    uint16_t* r2) {
   constexpr int TS = 64;         // slots per workgroup
   constexpr int G = D / 8;       // 16-byte groups per row
   constexpr int SPP = 256 / G;   // slots per pass
-  constexpr int LROW = D + 8;    // LDS row stride (elements)
-  __shared__ uint16_t tile[TS * LROW];
   __shared__ int32_t ids[TS];
 
   const int64_t BH = lv.B * lv.H;
@@ -171,8 +167,6 @@ __global__ __launch_bounds__(256) void gather_kernel(
     const Tin* x = which == 0 ? x0 : (which == 1 ? x1 : x2);
     const Tpool* px = which == 0 ? p0 : (which == 1 ? p1 : p2);
     uint16_t* ro = which == 0 ? r0 : (which == 1 ? r1 : r2);
-    uint16_t* to = which == 0 ? t0 : (which == 1 ? t1 : t2);
-    if (ro == nullptr && to == nullptr) continue;
 #pragma unroll
     for (int pass = 0; pass < TS / SPP; ++pass) {
       const int sl = sl0 + pass * SPP;
@@ -188,54 +182,43 @@ __global__ __launch_bounds__(256) void gather_kernel(
           load8_bf16(px + (b * lv.P1 + lv.poff[l] + j) * row + h * D + g * 8, val);
         }
       }
-      if (ro) *reinterpret_cast<uint4*>(ro + (bh * Sp + s0 + sl) * D + g * 8) = val;
-      *reinterpret_cast<uint4*>(&tile[sl * LROW + g * 8]) = val;
+      *reinterpret_cast<uint4*>(ro + (bh * Sp + s0 + sl) * D + g * 8) = val;
     }
-    __syncthreads();
-    if (to) {
-      // transposed: row d holds slots s0..s0+63; each thread writes 8 consecutive slots
-      for (int w = tid; w < D * (TS / 8); w += 256) {
-        const int d = w / (TS / 8);
-        const int sg = (w % (TS / 8)) * 8;
-        uint32_t pk[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          pk[u] = static_cast<uint32_t>(tile[swap23(sg + 2 * u) * LROW + d]) |
-                  (static_cast<uint32_t>(tile[swap23(sg + 2 * u + 1) * LROW + d]) << 16);
-        *reinterpret_cast<uint4*>(to + (bh * D + d) * Sp + s0 + sg) =
-            make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      }
-    }
-    __syncthreads();
   }
 }
 
 template <int D, typename Tin, typename Tpool>
 hipError_t gather_dispatch(const Levels& lv, int64_t Sp, const void* const x[3],
                            const void* const px[3], const int32_t* gmap, void* const rows[3],
-                           void* const trans[3], hipStream_t st) {
+                           hipStream_t st) {
   dim3 grid(static_cast<unsigned>(Sp / 64 * lv.B * lv.H));
   hipLaunchKernelGGL((gather_kernel<D, Tin, Tpool>), grid, dim3(256), 0, st, lv, Sp,
                      static_cast<const Tin*>(x[0]), static_cast<const Tin*>(x[1]),
                      static_cast<const Tin*>(x[2]), static_cast<const Tpool*>(px[0]),
                      static_cast<const Tpool*>(px[1]), static_cast<const Tpool*>(px[2]), gmap,
                      static_cast<uint16_t*>(rows[0]), static_cast<uint16_t*>(rows[1]),
-                     static_cast<uint16_t*>(rows[2]), static_cast<uint16_t*>(trans[0]),
-                     static_cast<uint16_t*>(trans[1]), static_cast<uint16_t*>(trans[2]));
+                     static_cast<uint16_t*>(rows[2]));
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t gather_d(const Levels& lv, int64_t Sp, int32_t in_f32, const void* const x[3],
                     const void* const px[3], int32_t pooled_f32, const int32_t* gmap,
-                    void* const rows[3], void* const trans[3], hipStream_t st) {
+                    void* const rows[3], hipStream_t st) {
   if (in_f32)
-    return pooled_f32
-               ? gather_dispatch<D, float, float>(lv, Sp, x, px, gmap, rows, trans, st)
-               : gather_dispatch<D, float, uint16_t>(lv, Sp, x, px, gmap, rows, trans, st);
-  return pooled_f32
-             ? gather_dispatch<D, uint16_t, float>(lv, Sp, x, px, gmap, rows, trans, st)
-             : gather_dispatch<D, uint16_t, uint16_t>(lv, Sp, x, px, gmap, rows, trans, st);
+    return pooled_f32 ? gather_dispatch<D, float, float>(lv, Sp, x, px, gmap, rows, st)
+                      : gather_dispatch<D, float, uint16_t>(lv, Sp, x, px, gmap, rows, st);
+  return pooled_f32 ? gather_dispatch<D, uint16_t, float>(lv, Sp, x, px, gmap, rows, st)
+                    : gather_dispatch<D, uint16_t, uint16_t>(lv, Sp, x, px, gmap, rows, st);
+}
+
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ x,
+                                                      uint16_t* __restrict__ y, int64_t n8) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  uint4 u;
+  load8_bf16(x + i * 8, u);
+  *reinterpret_cast<uint4*>(y + i * 8) = u;
 }
 
 }  // namespace
@@ -256,10 +239,17 @@ hipError_t launch_build_map(const Levels& lv, const int32_t* sel, int32_t* gmap,
 
 hipError_t launch_gather(const Levels& lv, int32_t in_f32, const void* x[3], const void* px[3],
                          int32_t pooled_f32, const int32_t* gmap, void* const rows[3],
-                         void* const trans[3], hipStream_t st) {
+                         hipStream_t st) {
   const int64_t Sp = padded_len(lv.S);
-  if (lv.D == 64) return gather_d<64>(lv, Sp, in_f32, x, px, pooled_f32, gmap, rows, trans, st);
-  return gather_d<128>(lv, Sp, in_f32, x, px, pooled_f32, gmap, rows, trans, st);
+  if (lv.D == 64) return gather_d<64>(lv, Sp, in_f32, x, px, pooled_f32, gmap, rows, st);
+  return gather_d<128>(lv, Sp, in_f32, x, px, pooled_f32, gmap, rows, st);
+}
+
+hipError_t launch_to_bf16(const float* x, void* y, int64_t n, hipStream_t st) {
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(to_bf16_kernel, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0,
+                     st, x, static_cast<uint16_t*>(y), n8);
+  return hipGetLastError();
 }
 
 }  // namespace lh

@@ -69,86 +69,10 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// ------------------------------------------------------------------------------------------
-// Operand-friendly layouts.
-//
-// Transposed tensors ([.., D, Sp]) store sequence position s at column swap23(s): bits 2 and 3
-// of s exchanged (an involution).  Within each group of 16 the stored order is
-// 0-3, 8-11, 4-7, 12-15, which is exactly the k order in which a C tile leaves an MFMA as the
-// next product's B operand (see c_to_op2): the matching A operand of lane l is then the single
-// 16-byte chunk 2*t + (l/32) of the row instead of two 8-byte pieces.
-__host__ __device__ __forceinline__ int64_t swap23(int64_t s) {
-  return (s & ~int64_t(12)) | ((s & 4) << 1) | ((s & 8) >> 1);
-}
-
-// LDS tiles are unpadded rows whose 16-byte chunks are XOR-swizzled.  The LDS serves a
-// 16-byte-per-lane read 16 lanes at a time from 64 four-byte banks, i.e. sixteen 16-byte bank
-// groups; the operand reads have 16 consecutive lanes on 16 consecutive rows at one logical
-// chunk, so the swizzle makes those 16 (row, chunk) pairs land in 16 different groups.  A
-// 128-byte row (64 bf16) fills half a bank line, so rows 2j and 2j+1 share the XOR key j;
-// a 256-byte row (128 bf16) fills a whole line and each of 16 rows gets its own key.
-template <int ROW_ELEMS>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  constexpr int CPR = ROW_ELEMS / 8;                // 16-byte chunks per row
-  constexpr int RPL = CPR >= 16 ? 1 : 16 / CPR;     // rows per 256-byte bank line
-  return chunk ^ ((row / RPL) % CPR);
-}
-
-// 16-byte MFMA operand: logical chunk `chunk` of `row` in a swizzled LDS tile.
-template <int ROW_ELEMS>
-__device__ __forceinline__ bf16x8 lds_op(const uint16_t* tile, int row, int chunk) {
-  return ld_op16(tile + row * ROW_ELEMS + (swz<ROW_ELEMS>(row, chunk) << 3));
-}
-
-// Byte offset of logical chunk 2j + l/32 in row lq of a swizzled tile of ROW_ELEMS bf16 per
-// row.  Row 32m + lq has row lq's XOR key (checked below), so its chunk sits
-// 64 * ROW_ELEMS * m bytes further: one per-lane offset per k step serves every 32-row block
-// of every tile of that shape, and the rest of the address is an instruction immediate.
-template <int ROW_ELEMS>
-__device__ __forceinline__ uint32_t lane_chunk_off(int lq, int hl, int j) {
-  constexpr int CPR = ROW_ELEMS / 8, RPL = CPR >= 16 ? 1 : 16 / CPR;  // as in swz
-  static_assert((32 / RPL) % CPR == 0, "rows lq and 32m + lq must share the XOR key");
-  return static_cast<uint32_t>(lq * ROW_ELEMS * 2 + (swz<ROW_ELEMS>(lq, 2 * j + hl) << 4));
-}
-
 // 16-byte MFMA operand at a byte offset into an LDS tile.
 __device__ __forceinline__ bf16x8 lds_at(const uint16_t* tile, uint32_t byte_off) {
   return ld_op16(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(tile) +
                                                    byte_off));
-}
-
-// Stage ROWS x ROW_ELEMS bf16 (row stride `gstride` elements in global memory) into a swizzled
-// LDS tile with gfx950 direct global->LDS loads: each wave instruction moves 64 x 16 bytes into
-// 1 KB of contiguous LDS, so lane l fetches the global chunk that belongs at LDS chunk
-// (instruction base + l).  No VGPRs hold the data; completion is tracked by vmcnt.  The lane's
-// byte offset from the (uniform) tile start is 32-bit, so the loads take the scalar-base +
-// 32-bit-offset form and keep no 64-bit address per lane; callers bound
-// (ROWS - 1) * gstride + ROW_ELEMS below 2^31 elements.
-template <int ROWS, int ROW_ELEMS, int NT>
-__device__ __forceinline__ void stage_tile(const uint16_t* g, int gstride, uint16_t* lds,
-                                           int tid) {
-  constexpr int CPR = ROW_ELEMS / 8;        // 16-byte chunks per row
-  constexpr int CHUNKS = ROWS * CPR;
-  static_assert(CHUNKS % NT == 0, "tile must be a whole number of 16-byte loads per thread");
-  const int wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int i = 0; i < CHUNKS / NT; ++i) {
-    const int base = (i * (NT / 64) + wave) * 64;  // first LDS chunk of this wave instruction
-    const int lin = base + lane;
-    const int row = lin / CPR, pc = lin % CPR;
-    const int c = swz<ROW_ELEMS>(row, pc);
-    uint32_t boff = static_cast<uint32_t>(row * gstride + c * 8) * 2u;
-    asm volatile("" : "+v"(boff));  // opaque: not re-associated with the tile base and hoisted
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(g) + boff, lds + base * 8, 16,
-                                     0, 0);
-  }
-}
-
-// 64 floats into LDS with one wave instruction (4 bytes per lane).
-__device__ __forceinline__ void stage_f32x64(const float* g, float* lds, int lane) {
-  uint32_t boff = 4u * lane;
-  asm volatile("" : "+v"(boff));
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(g) + boff, lds, 4, 0, 0);
 }
 
 // Lanes l and l ^ 32 exchange a value with one v_permlane32_swap (no LDS round trip); the

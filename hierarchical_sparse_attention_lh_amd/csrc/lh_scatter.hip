@@ -18,10 +18,9 @@
 // level's current contribution in registers (reloaded only when that level's entry
 // changes), so token rows are written whole and coarse rows are read once per run.
 // Scatter backward owns 64 slots of one head, sums each slot's token span in float32,
-// rounds once to bf16, writes the row layout directly and the transposed layout through
-// LDS, and fuses Delta = rowsum(dO * O) for the attention backward.
+// rounds once to bf16, writes the rows, and fuses Delta = rowsum(dO * O) for the attention
+// backward.
 #include "lh_internal.h"
-#include "lh_mfma.h"
 
 namespace lh {
 namespace {
@@ -183,12 +182,9 @@ __global__ __launch_bounds__(256) void scatter_kernel(Levels lv, int64_t Sp,
 template <int D, typename Tin>
 __global__ __launch_bounds__(256) void scatter_bwd_kernel(
     Levels lv, int64_t Sp, const int32_t* __restrict__ gmap, const float* __restrict__ og,
-    const Tin* __restrict__ dy, uint16_t* __restrict__ dog, uint16_t* __restrict__ dogt,
-    float* __restrict__ delta) {
+    const Tin* __restrict__ dy, uint16_t* __restrict__ dog, float* __restrict__ delta) {
   constexpr int G = D / 8, SPP = 256 / G;
-  constexpr int TS = 64;       // slots per workgroup (transposed writes are 128 B)
-  constexpr int LR = D + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t tile[TS * LR];
+  constexpr int TS = 64;  // slots per workgroup
   const int64_t BH = lv.B * lv.H;
   const int64_t bh = blockIdx.x % BH;  // heads fastest: neighbouring slot ranges of all heads
   const int64_t b = bh / lv.H, h = bh % lv.H;
@@ -232,28 +228,16 @@ __global__ __launch_bounds__(256) void scatter_bwd_kernel(
     float r[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) r[e] = bf16_to_f32(f32_to_bf16(acc[e]));
-    uint16_t* dst = dog + (bh * Sp + s) * D + g * 8;
-    st8(dst, r);
-    *reinterpret_cast<uint4*>(&tile[sl * LR + g * 8]) = *reinterpret_cast<const uint4*>(dst);
-    float o[8];
-    ld8(og + (bh * Sp + s) * D + g * 8, o);
+    st8(dog + (bh * Sp + s) * D + g * 8, r);
     float part = 0.f;
+    if (s < lv.S) {  // padding rows of og are never read
+      float o[8];
+      ld8(og + (bh * Sp + s) * D + g * 8, o);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) part = fmaf(r[e], o[e], part);
+      for (int e = 0; e < 8; ++e) part = fmaf(r[e], o[e], part);
+    }
     for (int m = 1; m < G; m <<= 1) part += __shfl_xor(part, m);
-    if (g == 0) delta[bh * Sp + s] = s < lv.S ? part : 0.f;
-  }
-  __syncthreads();
-  for (int w = threadIdx.x; w < D * (TS / 8); w += 256) {
-    const int d = w / (TS / 8);
-    const int sg = (w % (TS / 8)) * 8;
-    uint32_t pk[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      pk[u] = static_cast<uint32_t>(tile[swap23(sg + 2 * u) * LR + d]) |
-              (static_cast<uint32_t>(tile[swap23(sg + 2 * u + 1) * LR + d]) << 16);
-    *reinterpret_cast<uint4*>(dogt + (bh * D + d) * Sp + s0 + sg) =
-        make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    if (g == 0) delta[bh * Sp + s] = part;
   }
 }
 
@@ -308,17 +292,16 @@ hipError_t scatter_t(const Levels& lv, const int32_t* inv, const float* og, void
 
 template <typename Tin>
 hipError_t scatter_bwd_t(const Levels& lv, const int32_t* gmap, const float* og, const void* dy,
-                         void* dog, void* dogt, float* delta, hipStream_t st) {
+                         void* dog, float* delta, hipStream_t st) {
   const int64_t Sp = padded_len(lv.S);
   dim3 grid(static_cast<unsigned>(Sp / 64 * lv.B * lv.H));
   auto* a = static_cast<uint16_t*>(dog);
-  auto* at = static_cast<uint16_t*>(dogt);
   if (lv.D == 64)
     hipLaunchKernelGGL((scatter_bwd_kernel<64, Tin>), grid, dim3(256), 0, st, lv, Sp, gmap, og,
-                       static_cast<const Tin*>(dy), a, at, delta);
+                       static_cast<const Tin*>(dy), a, delta);
   else
     hipLaunchKernelGGL((scatter_bwd_kernel<128, Tin>), grid, dim3(256), 0, st, lv, Sp, gmap, og,
-                       static_cast<const Tin*>(dy), a, at, delta);
+                       static_cast<const Tin*>(dy), a, delta);
   return hipGetLastError();
 }
 
@@ -354,10 +337,10 @@ hipError_t launch_scatter(const Levels& lv, int32_t out_f32, const int32_t* inv,
 }
 
 hipError_t launch_scatter_bwd(const Levels& lv, int32_t in_f32, const int32_t* gmap,
-                              const float* og, const void* dy, void* dog, void* dogt,
-                              float* delta, hipStream_t st) {
-  return in_f32 ? scatter_bwd_t<float>(lv, gmap, og, dy, dog, dogt, delta, st)
-                : scatter_bwd_t<uint16_t>(lv, gmap, og, dy, dog, dogt, delta, st);
+                              const float* og, const void* dy, void* dog, float* delta,
+                              hipStream_t st) {
+  return in_f32 ? scatter_bwd_t<float>(lv, gmap, og, dy, dog, delta, st)
+                : scatter_bwd_t<uint16_t>(lv, gmap, og, dy, dog, delta, st);
 }
 
 hipError_t launch_gather_pool_bwd(const Levels& lv, int32_t out_f32, const int32_t* inv,

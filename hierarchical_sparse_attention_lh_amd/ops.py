@@ -12,7 +12,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import LH_BF16, LH_F32, LH_SEL_DIRECT, LH_SEL_REFINE, LhAttnDesc, LhConfig, LhGathered, LhPlanInfo, check
+from ._lib import LH_BF16, LH_F32, LH_SEL_DIRECT, LH_SEL_REFINE, LhAttnDesc, LhConfig, LhPlanInfo, check
 
 _TORCH_DTYPE = {LH_BF16: torch.bfloat16, LH_F32: torch.float32}
 
@@ -106,67 +106,94 @@ def lh_build_map(cfg, sel):
     return gmap, inv
 
 
-def lh_gather(cfg, q, k, v, pq, pk, pv, gmap, with_backward=True):
-    """Returns dict q, k, v ([B, H, Sp, D]) and qt, kt, vt ([B, H, D, Sp]), all bf16."""
+def lh_gather(cfg, q, k, v, pq, pk, pv, sel):
+    """Map and gathered rows in one call: returns (gmap, inv, {"q", "k", "v": [B, H, Sp, D] bf16})."""
     _check_tokens(cfg, q, k, v)
     info = lh_plan(cfg)
     sp, d = info.gathered_pad, cfg.head_dim
     dev = q.device
-    out = {}
-    for n in ("q", "k", "v", "qt", "kt", "vt"):
-        if not with_backward and n in ("v", "qt", "kt"):
-            out[n] = None
-            continue
-        shape = (cfg.batch, cfg.heads, d, sp) if n.endswith("t") else (cfg.batch, cfg.heads, sp, d)
-        out[n] = torch.empty(shape, dtype=torch.bfloat16, device=dev)
-    g = LhGathered(*[None if out[n] is None else out[n].data_ptr()
-                     for n in ("q", "k", "v", "qt", "kt", "vt")])
+    gmap = torch.empty((cfg.batch, cfg.heads, sp), dtype=torch.int32, device=dev)
+    inv = torch.empty((cfg.batch, cfg.heads, info.pyramid_total), dtype=torch.int32, device=dev)
+    out = {n: torch.empty((cfg.batch, cfg.heads, sp, d), dtype=torch.bfloat16, device=dev)
+           for n in "qkv"}
     code = LH_BF16 if pq is None or pq.dtype == torch.bfloat16 else LH_F32
     check(_lib.load().lh_gather(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(pq), _p(pk), _p(pv),
-                                code, _p(gmap), ctypes.byref(g), _stream()))
-    return out
+                                code, _p(sel), _p(gmap), _p(inv), _p(out["q"]), _p(out["k"]),
+                                _p(out["v"]), _stream()))
+    return gmap, inv, out
 
 
-def swap23_index(n: int, device=None):
-    """Column order of the library's transposed tensors: slot s sits at column swap23(s)
-    (bits 2 and 3 of s exchanged; an involution, so the same index maps both ways)."""
-    s = torch.arange(n, device=device)
-    return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1)
+_AXES = {"bhsd": (0, 1, 2), "bshd": (0, 2, 1)}  # tensor dims of (batch, head, position)
 
 
-def to_transposed(x):
-    """[..., Sp, D] -> [..., D, Sp] in the library's transposed layout (Sp a multiple of 16)."""
-    return x.transpose(-1, -2)[..., swap23_index(x.shape[-2], x.device)].contiguous()
+def attn_desc(q, k, v, o, causal=True, scale=0.0, layout="bhsd") -> LhAttnDesc:
+    """lh_attn_desc of torch tensors laid out [B, H, S, D] ("bhsd") or [B, S, H, D] ("bshd",
+    e.g. the layer's token tensors); strides come from the tensors themselves."""
+    ax = _AXES[layout]
+    b, h, s_, d = (q.shape[ax[0]], q.shape[ax[1]], q.shape[ax[2]], q.shape[3])
+    desc = LhAttnDesc()
+    desc.batch, desc.heads, desc.seq, desc.head_dim = b, h, s_, d
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", o)):
+        if t.stride(3) != 1:
+            raise ValueError("the last dimension must be contiguous")
+        st = getattr(desc, name)
+        for i in range(3):
+            st[i] = t.stride(ax[i])
+    desc.causal = 1 if causal else 0
+    desc.scale = scale
+    return desc
 
 
-def from_transposed(xt):
-    """Inverse of to_transposed."""
-    return xt[..., swap23_index(xt.shape[-1], xt.device)].transpose(-1, -2).contiguous()
+def _lse_shape(desc):
+    return (desc.batch, desc.heads, (desc.seq + 127) // 128 * 128)
 
 
-def attn_desc(batch, heads, seq, head_dim, scale=0.0) -> LhAttnDesc:
-    return LhAttnDesc(batch, heads, seq, head_dim, scale)
-
-
-def lh_attn_fwd(desc: LhAttnDesc, q, k, vt):
-    """q, k [B, H, Sp, D] bf16, vt [B, H, D, Sp] bf16 -> (o [B, H, Sp, D] f32, lse [B, H, Sp]);
-    lse is the base-2 log-sum-exp of each row (natural log-sum-exp times log2(e))."""
-    b, h, sp, d = q.shape
-    o = torch.empty((b, h, sp, d), dtype=torch.float32, device=q.device)
-    lse = torch.empty((b, h, sp), dtype=torch.float32, device=q.device)
-    check(_lib.load().lh_attn_fwd(ctypes.byref(desc), _p(q), _p(k), _p(vt), _p(o), _p(lse),
+def lh_attn_fwd(q, k, v, causal=True, scale=0.0, layout="bhsd"):
+    """Softmax attention over strided bf16 rows; returns (o float32 shaped like q, lse
+    [B, H, Sp] in base 2: the natural log-sum-exp times log2(e))."""
+    o = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    desc = attn_desc(q, k, v, o, causal, scale, layout)
+    lse = torch.empty(_lse_shape(desc), dtype=torch.float32, device=q.device)
+    check(_lib.load().lh_attn_fwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(o), _p(lse),
                                   _stream()))
     return o, lse
 
 
-def lh_attn_bwd(desc: LhAttnDesc, q, k, v, qt, kt, lse, delta, dout, doutt):
-    b, h, sp, d = q.shape
-    dq, dk, dv = (torch.empty((b, h, sp, d), dtype=torch.float32, device=q.device)
-                  for _ in range(3))
-    check(_lib.load().lh_attn_bwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(qt), _p(kt),
-                                  _p(lse), _p(delta), _p(dout), _p(doutt), _p(dq), _p(dk),
-                                  _p(dv), _stream()))
+def lh_attn_bwd(q, k, v, o, lse, dout, causal=True, scale=0.0, layout="bhsd"):
+    """Backward of lh_attn_fwd (dout bf16 laid out like o); returns float32 dq, dk, dv."""
+    desc = attn_desc(q, k, v, o, causal, scale, layout)
+    if dout.stride() != o.stride():
+        raise ValueError("dout must have the layout of o")
+    lib = _lib.load()
+    nbytes = ctypes.c_size_t(0)
+    check(lib.lh_attn_ws_bytes(ctypes.byref(desc), ctypes.byref(nbytes)))
+    ws = torch.empty(max(256, nbytes.value), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = (torch.empty(o.shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    check(lib.lh_attn_bwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(o), _p(lse), _p(dout),
+                          _p(dq), _p(dk), _p(dv), _p(ws), ws.numel(), _stream()))
     return dq, dk, dv
+
+
+def lh_attn_fwd_mapped(cfg, q, k, v, pq, pk, pv, gmap):
+    """The layer's attention with rows read through gmap: returns (og [B, H, Sp, D] float32,
+    lse [B, H, Sp]).  q, k, v are bf16 token tensors; pq/pk/pv bf16 pooled levels."""
+    info = lh_plan(cfg)
+    sp, d = info.gathered_pad, cfg.head_dim
+    og = torch.empty((cfg.batch, cfg.heads, sp, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((cfg.batch, cfg.heads, sp), dtype=torch.float32, device=q.device)
+    check(_lib.load().lh_attn_fwd_mapped(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(pq), _p(pk),
+                                         _p(pv), _p(gmap), _p(og), _p(lse), _stream()))
+    return og, lse
+
+
+def lh_attn_bwd_mapped(cfg, q, k, v, pq, pk, pv, gmap, lse, delta, dog, passes=3):
+    """Backward of lh_attn_fwd_mapped; returns float32 dqg, dkg, dvg [B, H, Sp, D]."""
+    shape = dog.shape
+    dqg, dkg, dvg = (torch.empty(shape, dtype=torch.float32, device=dog.device) for _ in range(3))
+    check(_lib.load().lh_attn_bwd_mapped(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(pq), _p(pk),
+                                         _p(pv), _p(gmap), _p(lse), _p(delta), _p(dog), _p(dqg),
+                                         _p(dkg), _p(dvg), passes, _stream()))
+    return dqg, dkg, dvg
 
 
 def lh_scatter(cfg, inv, og):
@@ -177,16 +204,16 @@ def lh_scatter(cfg, inv, og):
 
 
 def lh_scatter_bwd(cfg, gmap, og, dy):
+    """Returns (dog [B, H, Sp, D] bf16, delta [B, H, Sp] float32)."""
     _check_tokens(cfg, dy)
     info = lh_plan(cfg)
     sp, d = info.gathered_pad, cfg.head_dim
     dev = dy.device
     dog = torch.empty((cfg.batch, cfg.heads, sp, d), dtype=torch.bfloat16, device=dev)
-    dogt = torch.empty((cfg.batch, cfg.heads, d, sp), dtype=torch.bfloat16, device=dev)
     delta = torch.empty((cfg.batch, cfg.heads, sp), dtype=torch.float32, device=dev)
     check(_lib.load().lh_scatter_bwd(ctypes.byref(cfg), _p(gmap), _p(og), _p(dy), _p(dog),
-                                     _p(dogt), _p(delta), _stream()))
-    return dog, dogt, delta
+                                     _p(delta), _stream()))
+    return dog, delta
 
 
 def lh_gather_pool_bwd(cfg, inv, dqg, dkg, dvg):
@@ -209,7 +236,7 @@ class Buffers:
         self.ws_bwd = torch.empty(max(256, i.ws_backward_bytes), dtype=torch.uint8, device=device)
 
     def views(self):
-        """Typed views of the saved blob: gmap, inv, q, k, v, qt, kt, vt, o, lse."""
+        """Typed views of the saved blob: gmap, inv, pq, pk, pv, o, lse."""
         i, c = self.info, self.cfg
         b, h, d, sp, p = c.batch, c.heads, c.head_dim, i.gathered_pad, i.pyramid_total
 
@@ -217,16 +244,15 @@ class Buffers:
             nbytes = n * torch.tensor([], dtype=dtype).element_size()
             return self.saved[off:off + nbytes].view(dtype).view(shape)
 
+        pr = max(1, i.pooled_rows) if i.pooled_rows else 0
         out = {
             "gmap": view(i.saved_gmap, b * h * sp, torch.int32, (b, h, sp)),
             "inv": view(i.saved_inv, b * h * p, torch.int32, (b, h, p)),
             "o": view(i.saved_o, b * h * sp * d, torch.float32, (b, h, sp, d)),
             "lse": view(i.saved_lse, b * h * sp, torch.float32, (b, h, sp)),
         }
-        for n in ("q", "k", "v"):
-            out[n] = view(getattr(i, "saved_" + n), b * h * sp * d, torch.bfloat16, (b, h, sp, d))
-            out[n + "t"] = view(getattr(i, "saved_" + n + "t"), b * h * sp * d, torch.bfloat16,
-                                (b, h, d, sp))
+        for n in ("pq", "pk", "pv"):
+            out[n] = view(getattr(i, "saved_" + n), b * pr * h * d, torch.bfloat16, (b, pr, h, d))
         return out
 
 
@@ -250,14 +276,16 @@ def lh_forward_noalloc(cfg, q, k, v, y, saved):
     return y
 
 
-def lh_backward(cfg, bufs: Buffers, dy, dq=None, dk=None, dv=None):
-    """Layer backward with the selection lh_forward saved in `bufs`; returns dq, dk, dv."""
-    _check_tokens(cfg, dy, dq, dk, dv)
+def lh_backward(cfg, q, k, v, bufs: Buffers, dy, dq=None, dk=None, dv=None):
+    """Layer backward with the selection lh_forward saved in `bufs` (q, k, v: the forward's
+    inputs); returns dq, dk, dv."""
+    _check_tokens(cfg, q, k, v, dy, dq, dk, dv)
     dq = torch.empty_like(dy) if dq is None else dq
     dk = torch.empty_like(dy) if dk is None else dk
     dv = torch.empty_like(dy) if dv is None else dv
-    check(_lib.load().lh_backward(ctypes.byref(cfg), _p(bufs.saved), _p(dy), _p(dq), _p(dk),
-                                  _p(dv), _p(bufs.ws_bwd), bufs.ws_bwd.numel(), _stream()))
+    check(_lib.load().lh_backward(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(bufs.saved), _p(dy),
+                                  _p(dq), _p(dk), _p(dv), _p(bufs.ws_bwd), bufs.ws_bwd.numel(),
+                                  _stream()))
     return dq, dk, dv
 
 
@@ -266,10 +294,12 @@ class StagedLayer:
 
     Runs exactly the kernels lh_forward / lh_backward run, in the same order, so a caller
     can put timing events between stages.  `stages_fwd` / `stages_bwd` are lists of
-    (name, callable) pairs.
+    (name, callable) pairs.  bf16 layers only (a float32 layer also rounds its inputs).
     """
 
     def __init__(self, cfg: LhConfig, q, k, v, dy, device="cuda"):
+        if cfg.dtype != LH_BF16:
+            raise ValueError("StagedLayer runs bf16 layers")
         self.cfg = cfg
         self.info = i = lh_plan(cfg)
         c = cfg
@@ -282,43 +312,39 @@ class StagedLayer:
         self.sel = e((b, h, max(1, i.sel_total)), torch.int32)
         self.gmap = e((b, h, sp), torch.int32)
         self.inv = e((b, h, i.pyramid_total), torch.int32)
-        self.g = {n: e((b, h, d, sp) if n.endswith("t") else (b, h, sp, d), torch.bfloat16)
-                  for n in ("q", "k", "v", "qt", "kt", "vt")}
         self.og = e((b, h, sp, d), torch.float32)
         self.lse = e((b, h, sp), torch.float32)
         self.y = torch.empty_like(q)
         self.dog = e((b, h, sp, d), torch.bfloat16)
-        self.dogt = e((b, h, d, sp), torch.bfloat16)
         self.delta = e((b, h, sp), torch.float32)
         self.dxg = [e((b, h, sp, d), torch.float32) for _ in range(3)]
         self.dx = [torch.empty_like(q) for _ in range(3)]
-        self.desc = attn_desc(b, h, i.gathered_len, d)
-        self.gathered = LhGathered(*[self.g[n].data_ptr() for n in ("q", "k", "v", "qt", "kt", "vt")])
         lib = _lib.load()
         cr = ctypes.byref(cfg)
-        dr = ctypes.byref(self.desc)
         P = _p
-        g = self.g
         st = _stream
+        pools = (P(self.pq), P(self.pk), P(self.pv))
         self.stages_fwd = [
-            ("pool_score", lambda: lib.lh_pool_score(cr, P(q), P(k), P(v), P(self.pq), P(self.pk),
-                                                     P(self.pv), LH_BF16, P(self.scores), st())),
+            ("pool_score", lambda: lib.lh_pool_score(cr, P(q), P(k), P(v), *pools, LH_BF16,
+                                                     P(self.scores), st())),
             ("topk", lambda: lib.lh_topk(cr, P(self.scores), P(self.sel), st())),
             ("build_map", lambda: lib.lh_build_map(cr, P(self.sel), P(self.gmap), P(self.inv), st())),
-            ("gather", lambda: lib.lh_gather(cr, P(q), P(k), P(v), P(self.pq), P(self.pk), P(self.pv),
-                                             LH_BF16, P(self.gmap), ctypes.byref(self.gathered), st())),
-            ("attn_fwd", lambda: lib.lh_attn_fwd(dr, P(g["q"]), P(g["k"]), P(g["vt"]), P(self.og),
-                                                 P(self.lse), st())),
+            ("attn_fwd", lambda: lib.lh_attn_fwd_mapped(cr, P(q), P(k), P(v), *pools, P(self.gmap),
+                                                        P(self.og), P(self.lse), st())),
             ("scatter", lambda: lib.lh_scatter(cr, P(self.inv), P(self.og), P(self.y), st())),
         ]
-        bwd_args = lambda: (dr, P(g["q"]), P(g["k"]), P(g["v"]), P(g["qt"]), P(g["kt"]),  # noqa: E731
-                            P(self.lse), P(self.delta), P(self.dog), P(self.dogt),
-                            P(self.dxg[0]), P(self.dxg[1]), P(self.dxg[2]), st())
+
+        def bwd(passes):
+            return lambda: lib.lh_attn_bwd_mapped(cr, P(q), P(k), P(v), *pools, P(self.gmap),
+                                                  P(self.lse), P(self.delta), P(self.dog),
+                                                  P(self.dxg[0]), P(self.dxg[1]), P(self.dxg[2]),
+                                                  passes, st())
+
         self.stages_bwd = [
-            ("scatter_bwd", lambda: lib.lh_scatter_bwd(cr, P(self.gmap), P(self.og), P(dy), P(self.dog),
-                                                       P(self.dogt), P(self.delta), st())),
-            ("attn_bwd_dkdv", lambda: lib.lh_attn_bwd_dkdv(*bwd_args())),
-            ("attn_bwd_dq", lambda: lib.lh_attn_bwd_dq(*bwd_args())),
+            ("scatter_bwd", lambda: lib.lh_scatter_bwd(cr, P(self.gmap), P(self.og), P(dy),
+                                                       P(self.dog), P(self.delta), st())),
+            ("attn_bwd_dkdv", bwd(1)),
+            ("attn_bwd_dq", bwd(2)),
             ("gather_pool_bwd", lambda: lib.lh_gather_pool_bwd(cr, P(self.inv), P(self.dxg[0]),
                                                                P(self.dxg[1]), P(self.dxg[2]),
                                                                P(self.dx[0]), P(self.dx[1]),

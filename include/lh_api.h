@@ -52,14 +52,10 @@
  *     No entry point synchronises the host.  Calls on different streams that touch
  *     different buffers may run concurrently; the library's only mutable global state is
  *     the static workspace of lh_forward_noalloc (see there).
- *   - Tensors are dense and row-major.  Token tensors are [B, N, H, D].  Gathered-domain
- *     tensors store Sp = S rounded up to a multiple of 128 slots: rows [B, H, Sp, D],
- *     "transposed" [B, H, D, Sp], per-slot vectors [B, H, Sp].  In a transposed tensor,
- *     slot s sits at column swap23(s) = s with its bits 2 and 3 exchanged (within every
- *     group of 16 slots the stored order is 0-3, 8-11, 4-7, 12-15), the k order the MFMA
- *     operands consume.  Slots S..Sp-1 are padding;
- *     the library writes them as finite values (zeros), and callers of the attention entry
- *     points must do the same.
+ *   - Tensors are dense and row-major unless strides are given.  Token tensors are
+ *     [B, N, H, D].  Gathered-domain tensors store Sp = S rounded up to a multiple of 128
+ *     slots: rows [B, H, Sp, D], per-slot vectors [B, H, Sp].  Slots S..Sp-1 are padding;
+ *     the library writes them as finite values (zeros for gradients and Delta).
  *   - The forward and backward are deterministic (no atomics, fixed reduction orders).
  */
 #ifndef LH_API_H
@@ -143,16 +139,19 @@ typedef struct lh_plan_info {
   int64_t k_eff[LH_MAX_LEVELS];        /* min(k[l], n_l) at selected levels, else 0       */
   int64_t n_chunks[LH_MAX_LEVELS];     /* chunks at selected levels, else 0               */
   int64_t chunk_width[LH_MAX_LEVELS];  /* entries per chunk at selected levels            */
+  int64_t quota_base[LH_MAX_LEVELS];   /* every chunk of level l keeps quota_base[l] ...  */
+  int64_t quota_rem[LH_MAX_LEVELS];    /* ... plus one for chunks c < quota_rem[l]        */
   int64_t sel_offset[LH_MAX_LEVELS];   /* start of level l's kept indices in `sel`        */
   int64_t sel_total;                   /* sum_l k_eff[l]                                  */
   int64_t gathered_len;                /* S (the same for every batch and head)           */
   int64_t gathered_pad;                /* Sp = S rounded up to a multiple of 128: the
                                           stored length of every gathered-domain tensor  */
-  /* byte offsets of the pieces of the `saved` blob written by lh_forward */
-  size_t saved_gmap, saved_inv, saved_q, saved_k, saved_v, saved_qt, saved_kt, saved_vt,
-         saved_o, saved_lse;
+  /* byte offsets of the pieces of the `saved` blob written by lh_forward: the map (gmap
+     [B,H,Sp] and inv [B,H,P] int32), the pooled levels of Q, K, V ([B, pooled_rows, H, D]
+     bf16), the attention output Og ([B,H,Sp,D] float32) and its log-sum-exp ([B,H,Sp]) */
+  size_t saved_gmap, saved_inv, saved_pq, saved_pk, saved_pv, saved_o, saved_lse;
   size_t saved_bytes;                  /* size of the `saved` blob                        */
-  size_t ws_forward_bytes;             /* workspace lh_forward needs                      */
+  size_t ws_forward_bytes;             /* workspace lh_forward needs (scores, selection)  */
   size_t ws_backward_bytes;            /* workspace lh_backward needs                     */
   float softmax_scale;                 /* the scale actually used                         */
 } lh_plan_info;
@@ -195,67 +194,69 @@ lh_status lh_topk(const lh_config* cfg, const float* scores, int32_t* sel, lh_st
 lh_status lh_build_map(const lh_config* cfg, const int32_t* sel, int32_t* gmap, int32_t* inv,
                        lh_stream_t stream);
 
-/* The gathered tensors: device bfloat16; row layouts [B, H, Sp, D], transposed [B, H, D, Sp].
- * q, k and vt are what the forward attention reads; v, qt and kt are only needed by the
- * backward and may be NULL (skipped) for a forward-only call. */
-typedef struct lh_gathered {
-  void* q;
-  void* k;
-  void* v;
-  void* qt;
-  void* kt;
-  void* vt;
-} lh_gathered;
-
-/* Stage 4b: gather rows.  Slot s of head (b, h) receives the row of pyramid entry gmap[s]:
- * a raw token of q/k/v (level 0) or a pooled row of pq/pk/pv (level >= 1), rounded to
- * bfloat16; padding slots become zero rows.  q/k/v as in lh_pool_score; pq/pk/pv in
- * pooled_dtype (may be NULL when L = 1). */
+/* Stage 4 as one call: the map of lh_build_map, then the gathered rows.  Slot s of head
+ * (b, h) receives the row of pyramid entry gmap[s] -- a raw token of q/k/v (level 0) or a
+ * pooled row of pq/pk/pv (level >= 1) -- rounded to bfloat16; padding slots are zero rows.
+ *   q, k, v  as in lh_pool_score; pq, pk, pv in pooled_dtype (may be NULL when L = 1)
+ *   sel      device int32 [B, H, sel_total];  gmap, inv as in lh_build_map (written)
+ *   qg,kg,vg device bf16 [B, H, Sp, D] (written)
+ * lh_forward does not call this: its attention reads the same rows through gmap. */
 lh_status lh_gather(const lh_config* cfg, const void* q, const void* k, const void* v,
                     const void* pq, const void* pk, const void* pv, int32_t pooled_dtype,
-                    const int32_t* gmap, const lh_gathered* out, lh_stream_t stream);
+                    const int32_t* sel, int32_t* gmap, int32_t* inv, void* qg, void* kg,
+                    void* vg, lh_stream_t stream);
 
-/* Causal attention over a gathered sequence ([WS] item 3; [HE] news.hamidun.com,
- * "Nous Research introduced Lighthouse Attention ...", section "How Lighthouse Attention
- * Works": the layer wraps ordinary scaled dot-product attention). */
+/* Causal (or full) softmax attention ([WS] item 3; [HE] news.hamidun.com, "Nous Research
+ * introduced Lighthouse Attention ...", section "How Lighthouse Attention Works": the layer
+ * wraps ordinary scaled dot-product attention), over rows given by strides: element
+ * (b, h, s, d) of q is q[b*q_stride[0] + h*q_stride[1] + s*q_stride[2] + d] (d contiguous),
+ * likewise k, v and o.  Dense attention on [B, N, H, D] tensors uses strides
+ * (N*H*D, D, H*D); a gathered [B, H, S, D] tensor (H*S*D, S*D, D). */
 typedef struct lh_attn_desc {
-  int64_t batch, heads, seq, head_dim; /* B, H, S, D; D in {64, 128}; 1 <= S <= 2^24;
-                                          tensors hold Sp = S rounded up to 128 slots      */
+  int64_t batch, heads, seq, head_dim; /* B, H, S, D; D in {64, 128}; 1 <= S <= 2^24       */
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3]; /* elements, (b, h, s)   */
+  int32_t causal;                      /* 1: key s' <= query s; 0: every key             */
   float scale;                         /* <= 0 selects 1/sqrt(D)                        */
 } lh_attn_desc;
 
-/* Og[s] = sum_{s' <= s} softmax(scale * q[s].k[s']) v[s'];  lse[s] = log2 of
- * sum_{s' <= s} 2^(scale * log2(e) * q[s].k[s']), the row's log-sum-exp in base 2 (the natural
- * log-sum-exp times log2(e)): the statistic the backward passes consume directly.
- *   q, k device bf16 [B, H, Sp, D];  vt device bf16 [B, H, D, Sp]  (finite padding)
- *   o    device float32 [B, H, Sp, D];  lse device float32 [B, H, Sp]; padding rows get
- *        the (finite) result of attending over all S keys */
-lh_status lh_attn_fwd(const lh_attn_desc* desc, const void* q, const void* k, const void* vt,
+/* O[s] = sum_{s' <= s} softmax(scale * q[s].k[s']) v[s'] (all s' when causal = 0);
+ * lse[s] = log2 of sum_{s'} 2^(scale * log2(e) * q[s].k[s']), the row's log-sum-exp in base 2
+ * (the natural log-sum-exp times log2(e)).
+ *   q, k, v device bf16 rows (16-byte aligned, every stride a multiple of 8)
+ *   o       device float32 rows at o_stride; rows s < S are written
+ *   lse     device float32 [B, H, Sp] (Sp = S rounded up to 128; padding entries finite) */
+lh_status lh_attn_fwd(const lh_attn_desc* desc, const void* q, const void* k, const void* v,
                       float* o, float* lse, lh_stream_t stream);
 
-/* Backward of lh_attn_fwd for upstream gradient dout (bf16).  Needs Delta = rowsum(dout*o)
- * (float32 [B, H, S]; lh_scatter_bwd produces it).
- *   q, k, v device bf16 [B, H, Sp, D]; qt, kt device bf16 [B, H, D, Sp]
- *   lse, delta device float32 [B, H, Sp] (finite padding)
- *   dout device bf16 [B, H, Sp, D]; doutt device bf16 [B, H, D, Sp] (zero padding)
- *   dq, dk, dv device float32 [B, H, Sp, D] (overwritten; padding rows are zero) */
-lh_status lh_attn_bwd(const lh_attn_desc* desc, const void* q, const void* k, const void* v,
-                      const void* qt, const void* kt, const float* lse, const float* delta,
-                      const void* dout, const void* doutt, float* dq, float* dk, float* dv,
-                      lh_stream_t stream);
+/* Bytes of workspace lh_attn_bwd needs (Delta = rowsum(dO * O), float32 [B, H, Sp]). */
+lh_status lh_attn_ws_bytes(const lh_attn_desc* desc, size_t* bytes);
 
-/* The two passes lh_attn_bwd runs, exported separately (same arguments as lh_attn_bwd):
- * the key pass writes dk and dv (dK = scale dS^T Q, dV = P^T dO), the query pass writes dq
- * (dQ = scale dS K).  Arguments a pass does not read may be NULL (key pass: kt, dq; query
- * pass: qt, doutt, dk, dv). */
-lh_status lh_attn_bwd_dkdv(const lh_attn_desc* desc, const void* q, const void* k,
-                           const void* v, const void* qt, const void* kt, const float* lse,
-                           const float* delta, const void* dout, const void* doutt, float* dq,
-                           float* dk, float* dv, lh_stream_t stream);
-lh_status lh_attn_bwd_dq(const lh_attn_desc* desc, const void* q, const void* k, const void* v,
-                         const void* qt, const void* kt, const float* lse, const float* delta,
-                         const void* dout, const void* doutt, float* dq, float* dk, float* dv,
-                         lh_stream_t stream);
+/* Backward of lh_attn_fwd for the upstream gradient dout (bf16 rows at o_stride), from its
+ * o and lse: dV = P^T dO, dP = dO V^T, dS = P (dP - Delta), dQ = scale dS K, dK = scale dS^T Q.
+ *   dq, dk, dv device float32 rows at o_stride (rows s < S written); ws as above. */
+lh_status lh_attn_bwd(const lh_attn_desc* desc, const void* q, const void* k, const void* v,
+                      const float* o, const float* lse, const void* dout, float* dq, float* dk,
+                      float* dv, void* ws, size_t ws_bytes, lh_stream_t stream);
+
+/* The attention of the layer with its rows read through the map (no gathered copy): slot s
+ * of head (b, h) is pyramid entry gmap[s] of q/k/v (level 0) or pq/pk/pv (pooled levels,
+ * bf16, as written by lh_pool_score).  Causal, scale cfg->softmax_scale.
+ *   og  device float32 [B, H, Sp, D] (every slot written; padding rows finite)
+ *   lse device float32 [B, H, Sp] */
+lh_status lh_attn_fwd_mapped(const lh_config* cfg, const void* q, const void* k, const void* v,
+                             const void* pq, const void* pk, const void* pv,
+                             const int32_t* gmap, float* og, float* lse, lh_stream_t stream);
+
+/* Backward of lh_attn_fwd_mapped.  passes: 1 = key pass (dkg, dvg), 2 = query pass (dqg),
+ * 3 = both; an argument a selected pass does not write may be NULL.
+ *   lse, delta device float32 [B, H, Sp] (delta from lh_scatter_bwd)
+ *   dog        device bf16 [B, H, Sp, D] (from lh_scatter_bwd)
+ *   dqg, dkg, dvg device float32 [B, H, Sp, D] (padding rows zero) */
+lh_status lh_attn_bwd_mapped(const lh_config* cfg, const void* q, const void* k, const void* v,
+                             const void* pq, const void* pk, const void* pv,
+                             const int32_t* gmap, const float* lse, const float* delta,
+                             const void* dog, float* dqg, float* dkg, float* dvg, int32_t passes,
+                             lh_stream_t stream);
 
 /* Stage 5 ([EN] four-stage): Y[b, t, h] = sum_l og[b, h, inv(l, floor((t+1)/p^l) - 1)]
  * over gathered entries, one float32 sum, one rounding to cfg->dtype.
@@ -265,14 +266,12 @@ lh_status lh_scatter(const lh_config* cfg, const int32_t* inv, const float* og, 
                      lh_stream_t stream);
 
 /* Adjoint of lh_scatter: dOg[s] = sum of dY over the tokens slot s reached, rounded to
- * bf16 and written in row and transposed layouts; delta[s] = sum_d dOg[s, d] * og[s, d].
+ * bf16; delta[s] = sum_d dOg[s, d] * og[s, d] (the attention backward's Delta, fused here).
  *   gmap device int32 [B, H, Sp]; og device float32 [B, H, Sp, D]
  *   dy device [B, N, H, D] in cfg->dtype
- *   dog device bf16 [B, H, Sp, D]; dogt device bf16 [B, H, D, Sp]; delta device f32
- *   [B, H, Sp]; padding slots are written as zeros */
+ *   dog device bf16 [B, H, Sp, D]; delta device float32 [B, H, Sp]; padding slots zero */
 lh_status lh_scatter_bwd(const lh_config* cfg, const int32_t* gmap, const float* og,
-                         const void* dy, void* dog, void* dogt, float* delta,
-                         lh_stream_t stream);
+                         const void* dy, void* dog, float* delta, lh_stream_t stream);
 
 /* Adjoint of gather o pool ([EN] four-stage: gradients reach Q, K, V through the gathered
  * values only): dX[b, t, h] = sum_l [entry (l, floor(t/p^l)) gathered] dXg[slot] / p^l.
@@ -286,10 +285,10 @@ lh_status lh_gather_pool_bwd(const lh_config* cfg, const int32_t* inv, const flo
  * Whole layer
  * ------------------------------------------------------------------------------------- */
 
-/* Forward: stages 1-5.
+/* Forward: stages 1-5 (pool+score, top-K, map, attention through the map, scatter).
  *   q, k, v device [B, N, H, D] in cfg->dtype;  y device [B, N, H, D] in cfg->dtype
  *   saved   device blob of lh_plan_info.saved_bytes, written here and read by lh_backward
- *           (gmap, inv, the six gathered tensors, Og and LSE at the saved_* offsets)
+ *           (map, pooled levels, Og and LSE at the saved_* offsets)
  *   ws      device workspace of at least ws_forward_bytes (contents undefined after) */
 lh_status lh_forward(const lh_config* cfg, const void* q, const void* k, const void* v,
                      void* y, void* saved, void* ws, size_t ws_bytes, lh_stream_t stream);
@@ -306,11 +305,15 @@ lh_status lh_forward(const lh_config* cfg, const void* q, const void* k, const v
 lh_status lh_forward_noalloc(const lh_config* cfg, const void* q, const void* k, const void* v,
                              void* y, void* saved, lh_stream_t stream);
 
-/* Backward with the selection frozen at what lh_forward saved.
+/* Backward with the selection frozen at what lh_forward saved.  The attention rows are read
+ * again through the map, so the forward's inputs q, k, v are passed too (unchanged since
+ * lh_forward, as an autograd framework keeps them).
+ *   q, k, v device [B, N, H, D] in cfg->dtype; saved as written by lh_forward
  *   dy device [B, N, H, D] in cfg->dtype; dq, dk, dv device [B, N, H, D] in cfg->dtype
  *   ws device workspace of at least ws_backward_bytes */
-lh_status lh_backward(const lh_config* cfg, const void* saved, const void* dy, void* dq,
-                      void* dk, void* dv, void* ws, size_t ws_bytes, lh_stream_t stream);
+lh_status lh_backward(const lh_config* cfg, const void* q, const void* k, const void* v,
+                      const void* saved, const void* dy, void* dq, void* dk, void* dv, void* ws,
+                      size_t ws_bytes, lh_stream_t stream);
 
 #ifdef __cplusplus
 }

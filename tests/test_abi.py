@@ -51,10 +51,17 @@ def test_plan_matches_closed_forms(name):
     assert info.pyramid_total == sum(sizes)
     assert info.sel_total == sum(min(w.k, n) for n in sizes[1:])
     assert abs(info.softmax_scale - w.head_dim ** -0.5) < 1e-7
-    offs = [info.saved_gmap, info.saved_inv, info.saved_q, info.saved_k, info.saved_v,
-            info.saved_qt, info.saved_kt, info.saved_vt, info.saved_o, info.saved_lse]
+    offs = [info.saved_gmap, info.saved_inv, info.saved_pq, info.saved_pk, info.saved_pv,
+            info.saved_o, info.saved_lse]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert info.saved_bytes > info.saved_lse
+    # the saved blob holds no gathered copy of Q, K, V: map, pooled levels, Og and LSE only
+    pooled = w.batch * info.pooled_rows * w.heads * w.head_dim * 2
+    assert info.saved_pk - info.saved_pq >= pooled and info.saved_o - info.saved_pv >= pooled
+    for lv in range(1, w.levels):
+        nch = info.n_chunks[lv]
+        assert info.quota_base[lv] * nch + info.quota_rem[lv] == info.k_eff[lv]
+        assert 0 <= info.quota_rem[lv] < nch
 
 
 def _cfg(**kw):
@@ -112,6 +119,17 @@ def _call(name, *args):
     return getattr(_lib.load(), name)(*args)
 
 
+def _desc(seq=100, d=64, strides=None):
+    desc = _lib.LhAttnDesc()
+    desc.batch, desc.heads, desc.seq, desc.head_dim = 1, 1, seq, d
+    st = strides or (seq * d, seq * d, d)
+    for name in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        for i in range(3):
+            getattr(desc, name)[i] = st[i]
+    desc.causal = 1
+    return desc
+
+
 def test_entry_points_reject_bad_pointers_before_launch():
     cfg = _cfg()
     c = ctypes.byref(cfg)
@@ -126,29 +144,39 @@ def test_entry_points_reject_bad_pointers_before_launch():
     assert _call("lh_pool_score", c, ok, ok, ok, ok, ok, ok, 5, ok, st) == L["LH_ERR_DTYPE"]
     assert _call("lh_topk", c, null, ok, st) == L["LH_ERR_NULL"]
     assert _call("lh_build_map", c, ok, bad, ok, st) == L["LH_ERR_ALIGN"]
-    g = _lib.LhGathered(0x10000, 0x10000, None, None, None, None)
-    assert _call("lh_gather", c, ok, ok, ok, ok, ok, ok, 0, ok, ctypes.byref(g), st) == L["LH_ERR_NULL"]
-    assert _call("lh_gather", c, ok, ok, ok, ok, ok, ok, 0, ok, None, st) == L["LH_ERR_NULL"]
-    d = _lib.LhAttnDesc(1, 1, 100, 64, 0.0)
+    assert _call("lh_gather", c, ok, ok, ok, ok, ok, ok, 0, ok, ok, ok, ok, ok, null, st) == L["LH_ERR_NULL"]
+    assert _call("lh_gather", c, ok, ok, ok, ok, ok, ok, 0, null, ok, ok, ok, ok, ok, st) == L["LH_ERR_NULL"]
+    assert _call("lh_gather", c, ok, ok, ok, ok, ok, ok, 3, ok, ok, ok, ok, ok, ok, st) == L["LH_ERR_DTYPE"]
+    d = _desc()
     dd = ctypes.byref(d)
     assert _call("lh_attn_fwd", dd, ok, ok, ok, ok, bad, st) == L["LH_ERR_ALIGN"]
-    d2 = _lib.LhAttnDesc(1, 1, 0, 64, 0.0)
-    assert _call("lh_attn_fwd", ctypes.byref(d2), ok, ok, ok, ok, ok, st) == L["LH_ERR_SHAPE"]
-    d4 = _lib.LhAttnDesc(1, 1, 2**24 + 1, 64, 0.0)  # above the attention length bound
-    assert _call("lh_attn_fwd", ctypes.byref(d4), ok, ok, ok, ok, ok, st) == L["LH_ERR_SHAPE"]
-    d5 = _lib.LhAttnDesc(1, 1, 2**24, 64, 0.0)      # at the bound: reaches the pointer checks
-    assert _call("lh_attn_fwd", ctypes.byref(d5), ok, ok, ok, ok, bad, st) == L["LH_ERR_ALIGN"]
-    d3 = _lib.LhAttnDesc(1, 1, 10, 32, 0.0)
-    assert _call("lh_attn_fwd", ctypes.byref(d3), ok, ok, ok, ok, ok, st) == L["LH_ERR_DTYPE"]
-    args = [dd] + [ok] * 12 + [st]
-    args[6] = null
-    assert _call("lh_attn_bwd", *args) == L["LH_ERR_NULL"]
+    assert _call("lh_attn_fwd", ctypes.byref(_desc(seq=0)), ok, ok, ok, ok, ok, st) == L["LH_ERR_SHAPE"]
+    # above the attention length bound, and at it (reaches the pointer checks)
+    assert _call("lh_attn_fwd", ctypes.byref(_desc(seq=2**24 + 1)), ok, ok, ok, ok, ok, st) == L["LH_ERR_SHAPE"]
+    assert _call("lh_attn_fwd", ctypes.byref(_desc(seq=2**24)), ok, ok, ok, ok, bad, st) == L["LH_ERR_ALIGN"]
+    assert _call("lh_attn_fwd", ctypes.byref(_desc(d=32)), ok, ok, ok, ok, ok, st) == L["LH_ERR_DTYPE"]
+    # a row stride that breaks 16-byte alignment of the rows
+    assert _call("lh_attn_fwd", ctypes.byref(_desc(strides=(6400, 6400, 68))), ok, ok, ok, ok, ok,
+                 st) == L["LH_ERR_ALIGN"]
+    nbytes = ctypes.c_size_t(0)
+    assert _call("lh_attn_ws_bytes", dd, ctypes.byref(nbytes)) == 0 and nbytes.value >= 128 * 4
+    assert _call("lh_attn_bwd", dd, ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, nbytes.value - 1, st) == \
+        L["LH_ERR_WORKSPACE"]
+    assert _call("lh_attn_bwd", dd, ok, ok, ok, null, ok, ok, ok, ok, ok, ok, nbytes.value, st) == \
+        L["LH_ERR_NULL"]
+    assert _call("lh_attn_fwd_mapped", c, ok, ok, ok, ok, ok, ok, null, ok, ok, st) == L["LH_ERR_NULL"]
+    assert _call("lh_attn_bwd_mapped", c, ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, 4,
+                 st) == L["LH_ERR_UNSUPPORTED"]
+    assert _call("lh_attn_bwd_mapped", c, ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, null, ok, ok, 3,
+                 st) == L["LH_ERR_NULL"]
     assert _call("lh_scatter", c, ok, ok, bad, st) == L["LH_ERR_ALIGN"]
-    assert _call("lh_scatter_bwd", c, ok, ok, ok, ok, ok, null, st) == L["LH_ERR_NULL"]
+    assert _call("lh_scatter_bwd", c, ok, ok, ok, ok, null, st) == L["LH_ERR_NULL"]
     assert _call("lh_gather_pool_bwd", c, ok, ok, ok, ok, ok, ok, bad, st) == L["LH_ERR_ALIGN"]
     info = ops.lh_plan(cfg)
     assert _call("lh_forward", c, ok, ok, ok, ok, ok, ok, info.ws_forward_bytes - 1, st) == L["LH_ERR_WORKSPACE"]
-    assert _call("lh_backward", c, ok, ok, ok, ok, ok, ok, info.ws_backward_bytes - 1, st) == L["LH_ERR_WORKSPACE"]
+    assert _call("lh_backward", c, ok, ok, ok, ok, ok, ok, ok, ok, ok,
+                 info.ws_backward_bytes - 1, st) == L["LH_ERR_WORKSPACE"]
+    assert _call("lh_backward", c, null, ok, ok, ok, ok, ok, ok, ok, ok, 1 << 40, st) == L["LH_ERR_NULL"]
     assert _call("lh_forward", c, ok, ok, ok, null, ok, ok, 1 << 40, st) == L["LH_ERR_NULL"]
 
 
@@ -160,9 +188,10 @@ def test_status_strings():
 
 
 def test_forward_noalloc_rejects_workspace_above_scratch_before_launch():
-    # the 98K layer needs ~0.2 GB of forward workspace: more than the static scratch
-    w = synth.WORKLOADS["layer-98k"]
-    cfg = ops.config_for(w)
+    # the benchmark workloads fit the static scratch; 2^20 tokens x 16 heads do not
+    for w in synth.WORKLOADS.values():
+        assert ops.lh_plan(ops.config_for(w)).ws_forward_bytes <= _lib.NOALLOC_SCRATCH_BYTES
+    cfg = ops.make_config(1, 2**20, 16, 64, 4, 4, 4096, 1024)
     assert ops.lh_plan(cfg).ws_forward_bytes > _lib.NOALLOC_SCRATCH_BYTES
     ok = ctypes.c_void_p(0x10000)
     code = _call("lh_forward_noalloc", ctypes.byref(cfg), ok, ok, ok, ok, ok, None)

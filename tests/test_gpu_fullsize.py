@@ -69,7 +69,7 @@ def test_full_size_heads_against_oracle(name, heads):
     layer = ops.StagedLayer(cfg, t["q"], t["k"], t["v"], t["dy"])
     layer.run(layer.stages_fwd + layer.stages_bwd)
     y, bufs = ops.lh_forward(cfg, t["q"], t["k"], t["v"])
-    dq, dk, dv = ops.lh_backward(cfg, bufs, t["dy"])
+    dq, dk, dv = ops.lh_backward(cfg, t["q"], t["k"], t["v"], bufs, t["dy"])
     torch.cuda.synchronize()
     # the benchmarked staged path and the monolithic entry points are the same computation
     assert torch.equal(layer.y, y)

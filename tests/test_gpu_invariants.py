@@ -35,7 +35,7 @@ def _inputs(w):
 
 def _run(cfg, t):
     y, bufs = ops.lh_forward(cfg, t["q"], t["k"], t["v"])
-    g = ops.lh_backward(cfg, bufs, t["dy"])
+    g = ops.lh_backward(cfg, t["q"], t["k"], t["v"], bufs, t["dy"])
     torch.cuda.synchronize()
     return y, g
 

@@ -199,8 +199,9 @@ def test_map_and_gather(w):
     pq, pk, pv, sc = ops.lh_pool_score(cfg, t["q"], t["k"], t["v"], pooled_dtype=torch.float32)
     sel = ops.lh_topk(cfg, sc)
     gmap, inv = ops.lh_build_map(cfg, sel)
-    g = ops.lh_gather(cfg, t["q"], t["k"], t["v"], pq, pk, pv, gmap)
+    gmap2, inv2, g = ops.lh_gather(cfg, t["q"], t["k"], t["v"], pq, pk, pv, sel)
     torch.cuda.synchronize()
+    assert torch.equal(gmap, gmap2) and torch.equal(inv, inv2)
     sel_np, gmap_np, inv_np = sel.cpu().numpy(), gmap.cpu().numpy(), inv.cpu().numpy()
     S, Sp = info.gathered_len, info.gathered_pad
     sizes = [info.level_size[l] for l in range(w.levels)]
@@ -228,82 +229,128 @@ def test_map_and_gather(w):
                             rows.append(pooled[name][b, info.pooled_offset[lv] + j, h])
                     want = O.round_bf16(np.stack(rows))
                     got = f64(g[name][b, h, :S])
-                    got_t = f64(ops.from_transposed(g[name + "t"])[b, h, :S])
-                    assert np.array_equal(got, got_t)
                     diff = got != want
                     near += int(diff.sum())
                     if diff.any():  # only one bf16 step, only near a tie
                         step = np.abs(want[diff]) * 2.0**-7
                         assert np.all(np.abs(got[diff] - want[diff]) <= step * 1.001)
                     assert np.all(f64(g[name][b, h, S:]) == 0)
-                    assert np.all(f64(ops.from_transposed(g[name + "t"])[b, h, S:]) == 0)
     print(f"[{w.name}] gathered elements one bf16 step off (ties): {near}")
     assert near <= 3
 
 
 # ------------------------------------------------------------------------ attention
-def _attn_case(seq, d, heads=2, seed=0):
+def _attn_case(seq, d, heads=2, seed=0, batch=1):
+    """bf16 Q, K, V [B, H, S, D] with a lognormal per-position scale, exactly S rows."""
     rng = np.random.default_rng(seed)
-    sp = (seq + 127) // 128 * 128
     x = {}
     for n in "qkv":
-        a = np.zeros((1, heads, sp, d), np.float32)
-        a[:, :, :seq] = rng.standard_normal((1, heads, seq, d)).astype(np.float32) * \
-            np.exp(0.5 * rng.standard_normal((1, 1, seq, 1))).astype(np.float32)
+        a = rng.standard_normal((batch, heads, seq, d)).astype(np.float32) * \
+            np.exp(0.5 * rng.standard_normal((batch, 1, seq, 1))).astype(np.float32)
         x[n] = torch.from_numpy(a).to(torch.bfloat16)
-    return x, sp
+    return x
+
+
+def _check_fwd(o, lse, x, causal, bh_list, d):
+    for b, h in bh_list:
+        qq, kk, vv = (f64(x[n][b, h]) for n in "qkv")
+        ro, rl = O.causal_attention(qq, kk, vv, d ** -0.5, causal=causal)
+        bound, _ = O.causal_attention(qq, kk, np.abs(vv), d ** -0.5, causal=causal)
+        seq = qq.shape[0]
+        go, gl = f64(o[b, h]), f64(lse[b, h, :seq])
+        rl = rl / np.log(2.0)  # the kernel reports the log-sum-exp in base 2
+        # P enters as a bf16 hi/lo pair (relative error <= 2^-16): the rest is float32 rounding
+        err = np.abs(go - ro)
+        print(f"attn fwd S={seq} D={d} causal={causal} ({b},{h}): max |dO| {err.max():.2e}, "
+              f"worst err/bound {(err / bound).max():.2e}, max |dLSE| {np.abs(gl - rl).max():.2e}")
+        assert np.all(err <= 2.0**-13 * bound + 1e-6), (b, h, err.max())
+        assert np.all(np.abs(gl - rl) <= 1e-5 + 1e-6 * np.abs(rl))
+        assert np.all(np.isfinite(f64(lse[b, h])))
+
+
+def _check_bwd(grads, x, dout, causal, bh_list, d):
+    for b, h in bh_list:
+        qq, kk, vv, dd = (f64(t[b, h]) for t in (x["q"], x["k"], x["v"], dout))
+        ro, rl = O.causal_attention(qq, kk, vv, d ** -0.5, causal=causal)
+        ref = O.causal_attention_backward(qq, kk, vv, ro, rl, dd, d ** -0.5, causal=causal)
+        for name, got, r in zip(("dq", "dk", "dv"), grads, ref):
+            g = f64(got[b, h])
+            err = np.abs(g - r)
+            tol = 2e-2 + 2.0**-8 * np.abs(r)
+            print(f"attn bwd S={qq.shape[0]} D={d} causal={causal} ({b},{h}) {name}: max err "
+                  f"{err.max():.2e}, worst err/tol {(err / tol).max():.3f}")
+            assert np.all(err <= tol), (name, b, h, err.max(), np.abs(r).max())
 
 
 @pytest.mark.parametrize("seq,d", [(1, 64), (100, 64), (128, 64), (1000, 64), (777, 128), (2048, 128),
                                    (12000, 64), (8192, 128)])
 def test_attention_forward(seq, d):
-    x, sp = _attn_case(seq, d, seed=seq + d)
+    x = _attn_case(seq, d, seed=seq + d)
     q, k, v = (x[n].to(DEV) for n in "qkv")
-    vt = ops.to_transposed(v)
-    desc = ops.attn_desc(1, 2, seq, d)
-    o, lse = ops.lh_attn_fwd(desc, q, k, vt)
+    o, lse = ops.lh_attn_fwd(q, k, v)
     torch.cuda.synchronize()
-    for h in range(2):
-        qq, kk, vv = (f64(x[n][0, h, :seq]) for n in "qkv")
-        ro, rl = O.causal_attention(qq, kk, vv, d ** -0.5)
-        bound, _ = O.causal_attention(qq, kk, np.abs(vv), d ** -0.5)
-        go, gl = f64(o[0, h, :seq]), f64(lse[0, h, :seq])
-        rl = rl / np.log(2.0)  # the kernel reports the log-sum-exp in base 2
-        # P enters as a bf16 hi/lo pair (relative error <= 2^-16): the rest is float32 rounding
-        err = np.abs(go - ro)
-        print(f"attn fwd S={seq} D={d} h={h}: max |dO| {err.max():.2e}, worst err/bound "
-              f"{(err / bound).max():.2e}, max |dLSE| {np.abs(gl - rl).max():.2e}")
-        assert np.all(err <= 2.0**-13 * bound + 1e-6), (h, err.max())
-        assert np.all(np.abs(gl - rl) <= 1e-5 + 1e-6 * np.abs(rl))
-        assert np.all(np.isfinite(f64(o[0, h])))
+    _check_fwd(o, lse, x, True, [(0, 0), (0, 1)], d)
 
 
 @pytest.mark.parametrize("seq,d", [(100, 64), (1000, 64), (777, 128), (640, 64), (6000, 64)])
 def test_attention_backward(seq, d):
-    x, sp = _attn_case(seq, d, seed=seq * 3 + d)
+    x = _attn_case(seq, d, seed=seq * 3 + d)
     rng = np.random.default_rng(seq)
-    dout_np = np.zeros((1, 2, sp, d), np.float32)
-    dout_np[:, :, :seq] = rng.standard_normal((1, 2, seq, d))
-    dout = torch.from_numpy(dout_np).to(torch.bfloat16)
+    dout = torch.from_numpy(rng.standard_normal((1, 2, seq, d)).astype(np.float32)).to(torch.bfloat16)
     q, k, v, do = (t.to(DEV) for t in (x["q"], x["k"], x["v"], dout))
-    desc = ops.attn_desc(1, 2, seq, d)
-    o, lse = ops.lh_attn_fwd(desc, q, k, ops.to_transposed(v))
-    delta = (do.float() * o).sum(-1)
-    dq, dk, dv = ops.lh_attn_bwd(desc, q, k, v, ops.to_transposed(q), ops.to_transposed(k), lse,
-                                 delta, do, ops.to_transposed(do))
+    o, lse = ops.lh_attn_fwd(q, k, v)
+    grads = ops.lh_attn_bwd(q, k, v, o, lse, do)
     torch.cuda.synchronize()
-    for h in range(2):
-        qq, kk, vv, dd = (f64(t[0, h, :seq]) for t in (x["q"], x["k"], x["v"], dout))
-        ro, rl = O.causal_attention(qq, kk, vv, d ** -0.5)
-        rq, rk, rv = O.causal_attention_backward(qq, kk, vv, ro, rl, dd, d ** -0.5)
-        for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-            g = f64(got[0, h, :seq])
-            err = np.abs(g - ref)
-            tol = 2e-2 + 2.0**-8 * np.abs(ref)
-            print(f"attn bwd S={seq} D={d} h={h} {name}: max err {err.max():.2e}, worst err/tol "
-                  f"{(err / tol).max():.3f}")
-            assert np.all(err <= tol), (name, h, err.max(), np.abs(ref).max())
-            assert np.all(f64(got[0, h, seq:]) == 0)
+    _check_bwd(grads, x, dout, True, [(0, 0), (0, 1)], d)
+
+
+@pytest.mark.parametrize("seq,d,causal", [(1000, 64, False), (333, 128, False), (2500, 64, True),
+                                          (1111, 128, True)])
+def test_attention_on_token_layout(seq, d, causal):
+    """Dense attention straight on [B, N, H, D] token tensors (strides, no copy), batch 2,
+    three heads, causal and not."""
+    x = _attn_case(seq, d, heads=3, seed=seq + 7 * d, batch=2)
+    tok = {n: a.transpose(1, 2).contiguous().to(DEV) for n, a in x.items()}  # [B, N, H, D]
+    rng = np.random.default_rng(seq + 1)
+    dout = torch.from_numpy(rng.standard_normal((2, 3, seq, d)).astype(np.float32)).to(torch.bfloat16)
+    o, lse = ops.lh_attn_fwd(tok["q"], tok["k"], tok["v"], causal=causal, layout="bshd")
+    do_tok = dout.transpose(1, 2).contiguous().to(DEV)
+    grads = ops.lh_attn_bwd(tok["q"], tok["k"], tok["v"], o, lse, do_tok, causal=causal,
+                            layout="bshd")
+    torch.cuda.synchronize()
+    bh = [(0, 0), (1, 2)]
+    _check_fwd(o.transpose(1, 2), lse, x, causal, bh, d)
+    _check_bwd([g.transpose(1, 2) for g in grads], x, dout, causal, bh, d)
+
+
+@pytest.mark.parametrize("w", [TINY, RAGGED, WIDE, POOL3, DIRECT_P2, EMPTY_SEL, FULL_BUDGET],
+                         ids=lambda w: w.name)
+def test_attention_mapped(w):
+    """The layer's attention reading rows through gmap, against the oracle on the gathered
+    rows of the same (GPU) selection, forward and backward; and bit-identical to the strided
+    attention over lh_gather's copies of those rows."""
+    t, x = inputs(w)
+    cfg = ops.config_for(w)
+    info = ops.lh_plan(cfg)
+    S, D = info.gathered_len, w.head_dim
+    tb = {n: a.to(torch.bfloat16) for n, a in t.items()}  # bf16 token rows (f32 layers round)
+    pq, pk, pv, sc = ops.lh_pool_score(cfg, t["q"], t["k"], t["v"], pooled_dtype=torch.bfloat16)
+    sel = ops.lh_topk(cfg, sc)
+    gmap, inv, g = ops.lh_gather(cfg, tb["q"], tb["k"], tb["v"], pq, pk, pv, sel) if w.dtype == "bf16" \
+        else ops.lh_gather(cfg, t["q"], t["k"], t["v"], pq, pk, pv, sel)
+    og, lse = ops.lh_attn_fwd_mapped(cfg, tb["q"], tb["k"], tb["v"], pq, pk, pv, gmap)
+    dog, delta = ops.lh_scatter_bwd(cfg, gmap, og, t["dy"])
+    dqg, dkg, dvg = ops.lh_attn_bwd_mapped(cfg, tb["q"], tb["k"], tb["v"], pq, pk, pv, gmap, lse,
+                                           delta, dog)
+    rows = {n: g[n][:, :, :S] for n in "qkv"}
+    o2, lse2 = ops.lh_attn_fwd(rows["q"], rows["k"], rows["v"])
+    torch.cuda.synchronize()
+    assert torch.equal(og[:, :, :S], o2) and torch.equal(lse[:, :, :S], lse2[:, :, :S])
+    assert torch.all(dqg[:, :, S:] == 0) and torch.all(dkg[:, :, S:] == 0)
+    bh = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    xg = {n: rows[n] for n in "qkv"}
+    _check_fwd(og[:, :, :S], lse, xg, True, bh, D)
+    _check_bwd([a[:, :, :S] for a in (dqg, dkg, dvg)], xg, dog[:, :, :S], True, bh, D)
 
 
 # ------------------------------------------------------------------------ stage 5
@@ -321,7 +368,7 @@ def test_scatter_and_adjoints(w):
     og_np[:, :, :S] = rng.standard_normal((w.batch, w.heads, S, D))
     og = torch.from_numpy(og_np).to(DEV)
     y = ops.lh_scatter(cfg, inv, og)
-    dog, dogt, delta = ops.lh_scatter_bwd(cfg, gmap, og, t["dy"])
+    dog, delta = ops.lh_scatter_bwd(cfg, gmap, og, t["dy"])
     g3 = [torch.from_numpy(np.ascontiguousarray(np.roll(og_np, i, axis=-1))).to(DEV) for i in range(3)]
     dq, dk, dv = ops.lh_gather_pool_bwd(cfg, inv, *g3)
     torch.cuda.synchronize()
@@ -349,9 +396,7 @@ def test_scatter_and_adjoints(w):
                 mag = O.scatter_backward(np.abs(x["dy"][b, :, h].astype(np.float64)), glev, gidx, w.pool)
                 step = 2.0**-7 * np.maximum(np.abs(gd), np.abs(rdog))
                 assert np.all(np.abs(gd - rdog) <= step + 64 * 2.0**-24 * mag)
-            assert np.array_equal(f64(ops.from_transposed(dogt)[b, h, :S]), gd)
             assert np.all(f64(dog[b, h, S:]) == 0)
-            assert np.all(f64(ops.from_transposed(dogt)[b, h, S:]) == 0)
             rdelta = np.sum(gd * og_np[b, h, :S], axis=1)  # Delta of the GPU's own dOg
             assert np.allclose(f64(delta[b, h, :S]), rdelta, rtol=1e-5, atol=1e-5)
             assert np.all(f64(delta[b, h, S:]) == 0)
@@ -374,7 +419,7 @@ def test_layer_forward_backward(w):
     t, x = inputs(w)
     cfg = ops.config_for(w)
     y, bufs = ops.lh_forward(cfg, t["q"], t["k"], t["v"])
-    dq, dk, dv = ops.lh_backward(cfg, bufs, t["dy"])
+    dq, dk, dv = ops.lh_backward(cfg, t["q"], t["k"], t["v"], bufs, t["dy"])
     torch.cuda.synchronize()
     ry, st, (rq, rk, rv) = _oracle_layer(w, x)
     # the GPU's selection must be the oracle's (checked exactly: these inputs have no near ties)
@@ -399,7 +444,7 @@ def test_layer_medium_forward_backward():
     t, x = inputs(w)
     cfg = ops.config_for(w)
     y, bufs = ops.lh_forward(cfg, t["q"], t["k"], t["v"])
-    dq, dk, dv = ops.lh_backward(cfg, bufs, t["dy"])
+    dq, dk, dv = ops.lh_backward(cfg, t["q"], t["k"], t["v"], bufs, t["dy"])
     torch.cuda.synchronize()
     # two heads through the oracle (each head is independent)
     sub = {n: a[:, :, [0, 5]] for n, a in x.items()}
@@ -416,12 +461,12 @@ def test_forward_is_deterministic_and_ignores_stale_buffers():
     t, x = inputs(w)
     cfg = ops.config_for(w)
     y1, b1 = ops.lh_forward(cfg, t["q"], t["k"], t["v"])
-    g1 = ops.lh_backward(cfg, b1, t["dy"])
+    g1 = ops.lh_backward(cfg, t["q"], t["k"], t["v"], b1, t["dy"])
     b2 = ops.Buffers(cfg)
     for buf in (b2.saved, b2.ws_fwd, b2.ws_bwd):
         buf.view(torch.uint8).fill_(0xFF)  # NaN patterns everywhere
     y2, _ = ops.lh_forward(cfg, t["q"], t["k"], t["v"], bufs=b2)
-    g2 = ops.lh_backward(cfg, b2, t["dy"])
+    g2 = ops.lh_backward(cfg, t["q"], t["k"], t["v"], b2, t["dy"])
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     for a, b in zip(g1, g2):

@@ -28,12 +28,12 @@ def test_forward_noalloc_matches_forward_on_two_calls():
         info = ops.lh_plan(cfg)
         assert info.ws_forward_bytes <= _lib.NOALLOC_SCRATCH_BYTES
         y_ref, bufs = ops.lh_forward(cfg, t["q"], t["k"], t["v"])
-        g_ref = ops.lh_backward(cfg, bufs, t["dy"])
+        g_ref = ops.lh_backward(cfg, t["q"], t["k"], t["v"], bufs, t["dy"])
         b2 = ops.Buffers(cfg)
         b2.saved.fill_(0xFF)  # stale NaN patterns: everything read must be written first
         y = torch.full_like(t["q"], float("nan"))
         ops.lh_forward_noalloc(cfg, t["q"], t["k"], t["v"], y, b2.saved)
-        g = ops.lh_backward(cfg, b2, t["dy"])
+        g = ops.lh_backward(cfg, t["q"], t["k"], t["v"], b2, t["dy"])
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref)
         va, vb = bufs.views(), b2.views()
