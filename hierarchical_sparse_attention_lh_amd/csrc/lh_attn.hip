@@ -113,65 +113,113 @@ struct RowSrc {
   int64_t sb, sh, ss, psb, n0;
 };
 
+// One head's rows: row id at byte address x + id * rsb, plus `dp` when id >= n0 (dp moves the
+// address into the pooled levels: ph - n0 * rsb - xh, a uniform byte difference).
 struct HeadRows {
-  const uint16_t* x;
-  const uint16_t* p;
-  int64_t ss, n0;
+  const char* x;
+  int64_t dp;
+  int64_t n0;
+  uint32_t rsb;
 };
 
 __device__ __forceinline__ HeadRows head_rows(const RowSrc& r, int64_t b, int64_t h) {
   HeadRows o;
-  o.x = r.x + b * r.sb + h * r.sh;
-  o.p = r.px != nullptr ? r.px + b * r.psb + h * r.sh : nullptr;
-  o.ss = r.ss;
+  o.x = reinterpret_cast<const char*>(r.x + b * r.sb + h * r.sh);
+  o.rsb = static_cast<uint32_t>(r.ss * 2);
   o.n0 = r.n0;
+  o.dp = 0;
+  if (r.px != nullptr) {
+    const char* ph = reinterpret_cast<const char*>(r.px + b * r.psb + h * r.sh);
+    o.dp = (ph - o.x) - r.n0 * static_cast<int64_t>(o.rsb);
+  }
   return o;
 }
 
 __device__ __forceinline__ const uint16_t* row_ptr(const HeadRows& hr, int64_t id) {
-  return id < hr.n0 ? hr.x + id * hr.ss : hr.p + (id - hr.n0) * hr.ss;
+  const int64_t off = id * static_cast<int64_t>(hr.rsb) + (id >= hr.n0 ? hr.dp : 0);
+  return reinterpret_cast<const uint16_t*>(hr.x + off);
 }
 
-// Rows staged per lane for a ROWS x D tile (256 threads, 16 bytes per lane per load).
+// Staging of a ROWS x D tile by 256 threads, 16 bytes per lane per load: load i of wave w
+// fills LDS chunks (4i + w) * 64 .. + 63, i.e. rows (4i + w) * RPL .. + RPL - 1 (RPL = 64 / CPR
+// rows per load), lane l taking row (4i + w) * RPL + l / CPR, logical chunk l % CPR.  The
+// swizzle key of that row depends on w and l only (rkey is periodic in the row with period
+// RPL * 4 / gcd), so each lane needs one row index and one swizzled chunk offset for every
+// load of every tile; the rest of the address is uniform.
 template <int ROWS, int D>
 struct Tile {
   static constexpr int CPR = D / 8;
+  static constexpr int RPL = 64 / CPR;
   static constexpr int LOADS = ROWS * CPR / 256;
   static_assert(ROWS * CPR % 256 == 0, "tile must be a whole number of loads per thread");
-  // tile row of this lane's i-th load
-  __device__ static __forceinline__ int row(int i, int wave, int lane) {
-    return ((i * 4 + wave) * 64 + lane) / CPR;
-  }
 };
 
-// Row ids of the rows this lane stages for the tile starting at position row0: mapped ids
-// come from the LDS ring slot `ring` (padding slots hold -1 and read row 0); strided
-// positions past the sequence are clamped to its last row (their results are masked).
-template <int ROWS, int D, bool MAPPED>
-__device__ __forceinline__ void tile_ids(const int32_t* ring, int row0, int S, int wave, int lane,
-                                         int (&id)[Tile<ROWS, D>::LOADS]) {
+struct LaneStage {
+  uint32_t row;    // the lane's row within each load's RPL rows
+  uint32_t chunk;  // byte offset of the lane's swizzled 16-byte piece within its row
+};
+
+template <int D>
+__device__ __forceinline__ LaneStage lane_stage(int wave, int lane) {
+  constexpr int CPR = D / 8, RPL = 64 / CPR;
+  LaneStage ls;
+  ls.row = static_cast<uint32_t>(lane / CPR);
+  ls.chunk = static_cast<uint32_t>(((lane % CPR) ^ rkey<D>(wave * RPL + lane / CPR)) << 4);
+  return ls;
+}
+
+// LDS destination of load i: each wave instruction fills 1 KB of contiguous LDS.
+__device__ __forceinline__ uint16_t* lds_dst(uint16_t* lds, int i, int wave) {
+  return lds + (i * 4 + wave) * 64 * 8;
+}
+
+// Stage rows row0 .. row0 + ROWS - 1 of a strided operand.  A whole tile inside the sequence
+// is a uniform base plus one 32-bit lane offset (scalar-base loads, no per-load address
+// arithmetic); a tile that crosses the end clamps each row to S - 1.
+template <int ROWS, int D>
+__device__ __forceinline__ void stage_strided(const HeadRows& hr, const LaneStage& ls, int row0,
+                                              int S, uint16_t* lds, int wave) {
+  using T = Tile<ROWS, D>;
+  if (row0 + ROWS <= S) {
+    // the wave's and lane's share of the offset is a VGPR; the load's and tile's share uniform
+    uint32_t o = (wave * T::RPL + ls.row) * hr.rsb + ls.chunk;
+    asm volatile("" : "+v"(o));  // opaque: kept as a 32-bit offset from the uniform base
 #pragma unroll
-  for (int i = 0; i < Tile<ROWS, D>::LOADS; ++i) {
-    const int r = Tile<ROWS, D>::row(i, wave, lane);
-    if constexpr (MAPPED)
-      id[i] = max(ring[r], 0);
-    else
-      id[i] = min(row0 + r, S - 1);
+    for (int i = 0; i < T::LOADS; ++i) {
+      const char* base = hr.x + static_cast<int64_t>(row0 + i * 4 * T::RPL) * hr.rsb;
+      __builtin_amdgcn_global_load_lds(base + o, lds_dst(lds, i, wave), 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      const int row = min(row0 + (i * 4 + wave) * T::RPL + static_cast<int>(ls.row), S - 1);
+      const char* g = hr.x + static_cast<int64_t>(row) * hr.rsb + ls.chunk;
+      __builtin_amdgcn_global_load_lds(g, lds_dst(lds, i, wave), 16, 0, 0);
+    }
   }
 }
 
-// Direct global->LDS loads of ROWS rows into a swizzled tile: each wave instruction fills 1 KB
-// of contiguous LDS, so lane l fetches the global chunk that belongs at LDS chunk base + l.
+// Row ids of the lane's loads of the tile whose ids sit in LDS ring slot `ring` (padding
+// slots hold -1 and read row 0).
 template <int ROWS, int D>
-__device__ __forceinline__ void stage_rows(const HeadRows& hr, const int (&id)[Tile<ROWS, D>::LOADS],
-                                           uint16_t* lds, int wave, int lane) {
-  constexpr int CPR = D / 8;
+__device__ __forceinline__ void ids_of(const int32_t* ring, const LaneStage& ls, int wave,
+                                       int (&id)[Tile<ROWS, D>::LOADS]) {
+  using T = Tile<ROWS, D>;
+#pragma unroll
+  for (int i = 0; i < T::LOADS; ++i) id[i] = max(ring[(i * 4 + wave) * T::RPL + ls.row], 0);
+}
+
+template <int ROWS, int D>
+__device__ __forceinline__ void stage_mapped(const HeadRows& hr, const LaneStage& ls,
+                                             const int (&id)[Tile<ROWS, D>::LOADS], uint16_t* lds,
+                                             int wave) {
 #pragma unroll
   for (int i = 0; i < Tile<ROWS, D>::LOADS; ++i) {
-    const int base = (i * 4 + wave) * 64;
-    const int r = (base + lane) / CPR, pc = (base + lane) % CPR;
-    const uint16_t* g = row_ptr(hr, id[i]) + ((pc ^ rkey<D>(r)) << 3);
-    __builtin_amdgcn_global_load_lds(g, lds + base * 8, 16, 0, 0);
+    const uint64_t rel =
+        static_cast<uint64_t>(static_cast<uint32_t>(id[i])) * hr.rsb + ls.chunk;
+    const int64_t dp = id[i] >= hr.n0 ? hr.dp : 0;
+    const char* g = hr.x + static_cast<int64_t>(rel) + dp;
+    __builtin_amdgcn_global_load_lds(g, lds_dst(lds, i, wave), 16, 0, 0);
   }
 }
 
@@ -214,7 +262,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
   const int qt = nqt - 1 - static_cast<int>(item % nqt);  // far-from-diagonal (heavy) first
   const int64_t b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, lq = lane & 31;
+  const int wave = tid >> 6;
+  const int lane = tid & 63, hl = lane >> 5, lq = lane & 31;
   const int q0 = qt * BM;
   const int qw = q0 + wave * 32;
   const int myq = qw + lq;
@@ -246,11 +295,26 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
 #pragma unroll
     for (int sec = 0; sec < 2; ++sec) toff[db][sec] = tr_off<D>(lane, db, sec);
 
+  const LaneStage ls = lane_stage<D>(wave, lane);
   auto load_ids = [&](int t) {
     if constexpr (MAPPED)
       if (wave == 0 && t < nkt) stage_words(gm + t * BN, idr[t & 3], lane, BN);
   };
-  auto ids_of = [&](int t, int (&id)[NL]) { tile_ids<BN, D, MAPPED>(idr[t & 3], t * BN, S, wave, lane, id); };
+  // row ids of tile t (mapped) -- read from LDS before the step issues any load
+  auto get_ids = [&](int t, int (&id)[NL]) {
+    if constexpr (MAPPED) ids_of<BN, D>(idr[t & 3], ls, wave, id);
+    else
+#pragma unroll
+      for (int i = 0; i < NL; ++i) id[i] = 0;
+  };
+  auto stage_k = [&](int t, const int (&id)[NL], uint16_t* lds) {
+    if constexpr (MAPPED) stage_mapped<BN, D>(hk, ls, id, lds, wave);
+    else stage_strided<BN, D>(hk, ls, t * BN, S, lds, wave);
+  };
+  auto stage_v = [&](int t, const int (&id)[NL], uint16_t* lds) {
+    if constexpr (MAPPED) stage_mapped<BN, D>(hv, ls, id, lds, wave);
+    else stage_strided<BN, D>(hv, ls, t * BN, S, lds, wave);
+  };
 
   // S^T of one key tile: 32 keys x 32 queries per C block, two blocks.
   auto scores = [&](f32x16 (&sacc)[2], auto bufc) {
@@ -374,11 +438,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     constexpr bool odd = decltype(par)::value;
     int idk[NL], idv[NL];
     const bool sk = t + 2 < nkt, sv = t + 1 < nkt;
-    if (sk) ids_of(t + 2, idk);
-    if (sv) ids_of(t + 1, idv);
+    if (sk) get_ids(t + 2, idk);
+    if (sv) get_ids(t + 1, idv);
     load_ids(t + 3);
-    if (sk) stage_rows<BN, D>(hk, idk, odd ? ks1 : ks0, wave, lane);
-    if (sv) stage_rows<BN, D>(hv, idv, odd ? vs0 : vs1, wave, lane);
+    if (sk) stage_k(t + 2, idk, odd ? ks1 : ks0);
+    if (sv) stage_v(t + 1, idv, odd ? vs0 : vs1);
     const int k0 = t * BN;
     if ((causal && k0 + BN - 1 > qw) || k0 + BN > S)
       soft_pv(std::true_type{}, t, cur, nxt, par);
@@ -453,11 +517,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     constexpr bool B1 = decltype(bufc)::value;
     int id[NL];
     const bool nx = t + 1 < nkt;
-    if (nx) ids_of(t + 1, id);
+    if (nx) get_ids(t + 1, id);
     load_ids(t + 2);
     if (nx) {
-      stage_rows<BN, D>(hk, id, B1 ? ks0 : ks1, wave, lane);
-      stage_rows<BN, D>(hv, id, B1 ? vs0 : vs1, wave, lane);
+      stage_k(t + 1, id, B1 ? ks0 : ks1);
+      stage_v(t + 1, id, B1 ? vs0 : vs1);
     }
     const int k0 = t * BN;
     if ((causal && k0 + BN - 1 > qw) || k0 + BN > S)
@@ -476,11 +540,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     __syncthreads();
     {
       int id0[NL], id1[NL];
-      ids_of(0, id0);
-      if (nkt > 1) ids_of(1, id1);
-      stage_rows<BN, D>(hk, id0, ks0, wave, lane);
-      stage_rows<BN, D>(hv, id0, vs0, wave, lane);
-      if (nkt > 1) stage_rows<BN, D>(hk, id1, ks1, wave, lane);
+      get_ids(0, id0);
+      if (nkt > 1) get_ids(1, id1);
+      stage_k(0, id0, ks0);
+      stage_v(0, id0, vs0);
+      if (nkt > 1) stage_k(1, id1, ks1);
     }
     wait_vmem();
     __syncthreads();
@@ -498,9 +562,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     __syncthreads();
     {
       int id0[NL];
-      ids_of(0, id0);
-      stage_rows<BN, D>(hk, id0, ks0, wave, lane);
-      stage_rows<BN, D>(hv, id0, vs0, wave, lane);
+      get_ids(0, id0);
+      stage_k(0, id0, ks0);
+      stage_v(0, id0, vs0);
     }
     wait_vmem();
     __syncthreads();
@@ -584,7 +648,8 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
   const int ktile = static_cast<int>(item % nkt);  // small key tiles have the most work: first
   const int64_t b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, lq = lane & 31;
+  const int wave = tid >> 6;
+  const int lane = tid & 63, hl = lane >> 5, lq = lane & 31;
   const int K0 = ktile * BK;
   const int kw = K0 + wave * 32;
   const int mykey = kw + lq;
@@ -618,6 +683,12 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
   const int qt0 = causal ? K0 / BQ : 0;
   const int nqt = (S + BQ - 1) / BQ;
 
+  HeadRows hd;  // dO rows (strided)
+  hd.x = reinterpret_cast<const char*>(dob);
+  hd.rsb = static_cast<uint32_t>(a.dss * 2);
+  hd.n0 = int64_t(1) << 62;
+  hd.dp = 0;
+  const LaneStage ls = lane_stage<D>(wave, lane);
   auto load_ids = [&](int t) {
     if constexpr (MAPPED)
       if (wave == 0 && t < nqt) stage_words(gm + t * BQ, idr[t & 3], lane, BQ);
@@ -627,18 +698,14 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
   auto stage = [&](int t, auto bufc) {
     constexpr bool B1 = decltype(bufc)::value;
     const int q0 = t * BQ;
-    int id[NL], ido[NL];
-    tile_ids<BQ, D, MAPPED>(idr[t & 3], q0, S, wave, lane, id);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) ido[i] = min(q0 + QT::row(i, wave, lane), S - 1);
+    int id[NL];
+    if constexpr (MAPPED) ids_of<BQ, D>(idr[t & 3], ls, wave, id);
     load_ids(t + 1);
-    stage_rows<BQ, D>(hq, id, B1 ? qs1 : qs0, wave, lane);
-    HeadRows hd;
-    hd.x = dob;
-    hd.p = nullptr;
-    hd.ss = a.dss;
-    hd.n0 = int64_t(1) << 62;
-    stage_rows<BQ, D>(hd, ido, B1 ? ds1 : ds0, wave, lane);
+    if constexpr (MAPPED)
+      stage_mapped<BQ, D>(hq, ls, id, B1 ? qs1 : qs0, wave);
+    else
+      stage_strided<BQ, D>(hq, ls, q0, S, B1 ? qs1 : qs0, wave);
+    stage_strided<BQ, D>(hd, ls, q0, S, B1 ? ds1 : ds0, wave);
     if (wave == 0) stage_words(lb + q0, B1 ? ls1 : ls0, lane, BQ);
     if (wave == 1) stage_words(dlb + q0, B1 ? dl1 : dl0, lane, BQ);
   };
@@ -982,7 +1049,8 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
   const int qtile = nqt - 1 - static_cast<int>(item % nqt);
   const int64_t b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, lq = lane & 31;
+  const int wave = tid >> 6;
+  const int lane = tid & 63, hl = lane >> 5, lq = lane & 31;
   const int Q0 = qtile * BM;
   const int qw = Q0 + wave * 32;
   const int myq = qw + lq;
@@ -1015,6 +1083,7 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) koff[j] = op_off<D>(lq, hl, j);
 
+  const LaneStage ls = lane_stage<D>(wave, lane);
   auto load_ids = [&](int t) {
     if constexpr (MAPPED)
       if (wave == 0 && t < nkt) stage_words(gm + t * BN, idr[t & 3], lane, BN);
@@ -1022,10 +1091,15 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
   auto stage = [&](int t, auto bufc) {
     constexpr bool B1 = decltype(bufc)::value;
     int id[NL];
-    tile_ids<BN, D, MAPPED>(idr[t & 3], t * BN, S, wave, lane, id);
+    if constexpr (MAPPED) ids_of<BN, D>(idr[t & 3], ls, wave, id);
     load_ids(t + 1);
-    stage_rows<BN, D>(hk, id, B1 ? ks1 : ks0, wave, lane);
-    stage_rows<BN, D>(hv, id, B1 ? vs1 : vs0, wave, lane);
+    if constexpr (MAPPED) {
+      stage_mapped<BN, D>(hk, ls, id, B1 ? ks1 : ks0, wave);
+      stage_mapped<BN, D>(hv, ls, id, B1 ? vs1 : vs0, wave);
+    } else {
+      stage_strided<BN, D>(hk, ls, t * BN, S, B1 ? ks1 : ks0, wave);
+      stage_strided<BN, D>(hv, ls, t * BN, S, B1 ? vs1 : vs0, wave);
+    }
   };
 
   auto tile = [&](auto masked, int t, auto bufc) {

@@ -471,3 +471,18 @@ def test_forward_is_deterministic_and_ignores_stale_buffers():
     assert torch.equal(y1, y2)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+def test_dense_attention_32k_token_layout():
+    """Dense causal attention as its own operation at N = 32,768 (the stage-2 dense-resumption
+    call): straight on [B, N, H, D] token tensors of the medium workload's shape and values,
+    forward and backward, two of eight heads against the oracle."""
+    w = MEDIUM
+    t, x = inputs(w)
+    o, lse = ops.lh_attn_fwd(t["q"], t["k"], t["v"], layout="bshd")
+    grads = ops.lh_attn_bwd(t["q"], t["k"], t["v"], o, lse, t["dy"], layout="bshd")
+    torch.cuda.synchronize()
+    xb = {n: torch.from_numpy(x[n]).transpose(1, 2) for n in ("q", "k", "v", "dy")}  # [B, H, N, D]
+    heads = [(0, 0), (0, 5)]
+    _check_fwd(o.transpose(1, 2), lse, xb, True, heads, w.head_dim)
+    _check_bwd([g.transpose(1, 2) for g in grads], xb, xb["dy"], True, heads, w.head_dim)
