@@ -117,9 +117,12 @@ struct RowSrc {
 // address into the pooled levels: ph - n0 * rsb - xh, a uniform byte difference).
 struct HeadRows {
   const char* x;
-  int64_t dp;
+  const char* pn;  // mapped: the pooled rows' base moved back by n0 rows, so that row id >= n0
+                   // sits at pn + id * rsb, like a raw row at x + id * rsb
+  int64_t dp;      // pn - x
   int64_t n0;
   uint32_t rsb;
+  uint32_t n0b;    // n0 * rsb when the pyramid's rows span less than 4 GiB (32-bit offsets)
 };
 
 __device__ __forceinline__ HeadRows head_rows(const RowSrc& r, int64_t b, int64_t h) {
@@ -128,9 +131,13 @@ __device__ __forceinline__ HeadRows head_rows(const RowSrc& r, int64_t b, int64_
   o.rsb = static_cast<uint32_t>(r.ss * 2);
   o.n0 = r.n0;
   o.dp = 0;
+  o.pn = o.x;
+  o.n0b = 0;
   if (r.px != nullptr) {
     const char* ph = reinterpret_cast<const char*>(r.px + b * r.psb + h * r.sh);
     o.dp = (ph - o.x) - r.n0 * static_cast<int64_t>(o.rsb);
+    o.pn = o.x + o.dp;
+    o.n0b = static_cast<uint32_t>(r.n0 * o.rsb);
   }
   return o;
 }
@@ -209,6 +216,7 @@ __device__ __forceinline__ void ids_of(const int32_t* ring, const LaneStage& ls,
   for (int i = 0; i < T::LOADS; ++i) id[i] = max(ring[(i * 4 + wave) * T::RPL + ls.row], 0);
 }
 
+// Mapped rows, MODE 2: any pyramid size (64-bit address arithmetic per load).
 template <int ROWS, int D>
 __device__ __forceinline__ void stage_mapped(const HeadRows& hr, const LaneStage& ls,
                                              const int (&id)[Tile<ROWS, D>::LOADS], uint16_t* lds,
@@ -220,6 +228,32 @@ __device__ __forceinline__ void stage_mapped(const HeadRows& hr, const LaneStage
     const int64_t dp = id[i] >= hr.n0 ? hr.dp : 0;
     const char* g = hr.x + static_cast<int64_t>(rel) + dp;
     __builtin_amdgcn_global_load_lds(g, lds_dst(lds, i, wave), 16, 0, 0);
+  }
+}
+
+// Mapped rows, MODE 1 (the pyramid's rows span less than 4 GiB): the lane's 32-bit offsets
+// id * rsb + chunk, computed once per tile and shared by every operand with the same row
+// stride; each load is issued from the raw base for offsets below n0 * rsb and from the
+// moved pooled base otherwise.
+template <int ROWS, int D>
+__device__ __forceinline__ void mapped_offsets(const int* id, uint32_t rsb, const LaneStage& ls,
+                                               uint32_t* o) {
+#pragma unroll
+  for (int i = 0; i < Tile<ROWS, D>::LOADS; ++i) {
+    o[i] = static_cast<uint32_t>(id[i]) * rsb + ls.chunk;
+    asm volatile("" : "+v"(o[i]));
+  }
+}
+
+template <int ROWS, int D>
+__device__ __forceinline__ void stage_mapped32(const HeadRows& hr, const uint32_t* o,
+                                               uint16_t* lds, int wave) {
+#pragma unroll
+  for (int i = 0; i < Tile<ROWS, D>::LOADS; ++i) {
+    // (the instruction offset of a direct global->LDS load moves the LDS address too, so it
+    // stays 0 everywhere)
+    const char* base = o[i] < hr.n0b ? hr.x : hr.pn;
+    __builtin_amdgcn_global_load_lds(base + o[i], lds_dst(lds, i, wave), 16, 0, 0);
   }
 }
 
@@ -244,8 +278,10 @@ struct FwdArgs {
   float sl2;                  // scale * log2(e)
 };
 
-template <int D, bool PIPE, bool MAPPED>
+// MODE: 0 = strided rows, 1 = mapped rows with 32-bit offsets, 2 = mapped rows, 64-bit.
+template <int D, bool PIPE, int MODE>
 __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
+  constexpr bool MAPPED = MODE != 0;
   constexpr int BM = 128, BN = 64;
   using KT = Tile<BN, D>;
   constexpr int NL = KT::LOADS;
@@ -308,13 +344,18 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
       for (int i = 0; i < NL; ++i) id[i] = 0;
   };
   auto stage_k = [&](int t, const int (&id)[NL], uint16_t* lds) {
-    if constexpr (MAPPED) stage_mapped<BN, D>(hk, ls, id, lds, wave);
+    if constexpr (MODE == 2) stage_mapped<BN, D>(hk, ls, id, lds, wave);
     else stage_strided<BN, D>(hk, ls, t * BN, S, lds, wave);
   };
   auto stage_v = [&](int t, const int (&id)[NL], uint16_t* lds) {
-    if constexpr (MAPPED) stage_mapped<BN, D>(hv, ls, id, lds, wave);
+    if constexpr (MODE == 2) stage_mapped<BN, D>(hv, ls, id, lds, wave);
     else stage_strided<BN, D>(hv, ls, t * BN, S, lds, wave);
   };
+  // MODE 1: offsets of the tile whose V rows the next step stages (its K rows were staged
+  // with the same offsets one step earlier)
+  uint32_t vo[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) vo[i] = 0;
 
   // S^T of one key tile: 32 keys x 32 queries per C block, two blocks.
   auto scores = [&](f32x16 (&sacc)[2], auto bufc) {
@@ -436,13 +477,24 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
   // before this step issues any load, so no read waits on a load still in flight.
   auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto par) {
     constexpr bool odd = decltype(par)::value;
-    int idk[NL], idv[NL];
     const bool sk = t + 2 < nkt, sv = t + 1 < nkt;
-    if (sk) get_ids(t + 2, idk);
-    if (sv) get_ids(t + 1, idv);
-    load_ids(t + 3);
-    if (sk) stage_k(t + 2, idk, odd ? ks1 : ks0);
-    if (sv) stage_v(t + 1, idv, odd ? vs0 : vs1);
+    if constexpr (MODE == 1) {
+      int idk[NL];
+      if (sk) get_ids(t + 2, idk);
+      load_ids(t + 3);
+      if (sv) stage_mapped32<BN, D>(hv, vo, odd ? vs0 : vs1, wave);
+      if (sk) {
+        mapped_offsets<BN, D>(idk, hk.rsb, ls, vo);
+        stage_mapped32<BN, D>(hk, vo, odd ? ks1 : ks0, wave);
+      }
+    } else {
+      int idk[NL], idv[NL];
+      if (sk) get_ids(t + 2, idk);
+      if (sv) get_ids(t + 1, idv);
+      load_ids(t + 3);
+      if (sk) stage_k(t + 2, idk, odd ? ks1 : ks0);
+      if (sv) stage_v(t + 1, idv, odd ? vs0 : vs1);
+    }
     const int k0 = t * BN;
     if ((causal && k0 + BN - 1 > qw) || k0 + BN > S)
       soft_pv(std::true_type{}, t, cur, nxt, par);
@@ -520,8 +572,15 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     if (nx) get_ids(t + 1, id);
     load_ids(t + 2);
     if (nx) {
-      stage_k(t + 1, id, B1 ? ks0 : ks1);
-      stage_v(t + 1, id, B1 ? vs0 : vs1);
+      if constexpr (MODE == 1) {
+        uint32_t o[NL];
+        mapped_offsets<BN, D>(id, hk.rsb, ls, o);
+        stage_mapped32<BN, D>(hk, o, B1 ? ks0 : ks1, wave);
+        stage_mapped32<BN, D>(hv, o, B1 ? vs0 : vs1, wave);
+      } else {
+        stage_k(t + 1, id, B1 ? ks0 : ks1);
+        stage_v(t + 1, id, B1 ? vs0 : vs1);
+      }
     }
     const int k0 = t * BN;
     if ((causal && k0 + BN - 1 > qw) || k0 + BN > S)
@@ -542,9 +601,20 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
       int id0[NL], id1[NL];
       get_ids(0, id0);
       if (nkt > 1) get_ids(1, id1);
-      stage_k(0, id0, ks0);
-      stage_v(0, id0, vs0);
-      if (nkt > 1) stage_k(1, id1, ks1);
+      if constexpr (MODE == 1) {
+        uint32_t o0[NL];
+        mapped_offsets<BN, D>(id0, hk.rsb, ls, o0);
+        stage_mapped32<BN, D>(hk, o0, ks0, wave);
+        stage_mapped32<BN, D>(hv, o0, vs0, wave);
+        if (nkt > 1) {
+          mapped_offsets<BN, D>(id1, hk.rsb, ls, vo);
+          stage_mapped32<BN, D>(hk, vo, ks1, wave);
+        }
+      } else {
+        stage_k(0, id0, ks0);
+        stage_v(0, id0, vs0);
+        if (nkt > 1) stage_k(1, id1, ks1);
+      }
     }
     wait_vmem();
     __syncthreads();
@@ -563,8 +633,15 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     {
       int id0[NL];
       get_ids(0, id0);
-      stage_k(0, id0, ks0);
-      stage_v(0, id0, vs0);
+      if constexpr (MODE == 1) {
+        uint32_t o0[NL];
+        mapped_offsets<BN, D>(id0, hk.rsb, ls, o0);
+        stage_mapped32<BN, D>(hk, o0, ks0, wave);
+        stage_mapped32<BN, D>(hv, o0, vs0, wave);
+      } else {
+        stage_k(0, id0, ks0);
+        stage_v(0, id0, vs0);
+      }
     }
     wait_vmem();
     __syncthreads();
@@ -593,15 +670,17 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
 
 // Two waves per SIMD: the pipelined loop at D = 64, the plain loop at D = 128 (the pipeline's
 // extra registers would force one wave there, which cannot hide its vector work).
-#define LH_FWD(NAME, D, PIPE, MAPPED)                                                        \
+#define LH_FWD(NAME, D, PIPE, MODE)                                                          \
   __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void NAME( \
       FwdArgs a) {                                                                          \
-    attn_fwd_body<D, PIPE, MAPPED>(a);                                                      \
+    attn_fwd_body<D, PIPE, MODE>(a);                                                        \
   }
-LH_FWD(attn_fwd_d64, 64, true, false)
-LH_FWD(attn_fwd_d128, 128, false, false)
-LH_FWD(attn_fwd_mapped_d64, 64, true, true)
-LH_FWD(attn_fwd_mapped_d128, 128, false, true)
+LH_FWD(attn_fwd_d64, 64, true, 0)
+LH_FWD(attn_fwd_d128, 128, false, 0)
+LH_FWD(attn_fwd_mapped_d64, 64, true, 1)
+LH_FWD(attn_fwd_mapped_d128, 128, false, 1)
+LH_FWD(attn_fwd_mapped64_d64, 64, true, 2)
+LH_FWD(attn_fwd_mapped64_d128, 128, false, 2)
 #undef LH_FWD
 
 // ------------------------------------------------------------------------ backward
@@ -628,8 +707,9 @@ struct BwdArgs {
 // the staged dO and Q row tiles.  V is negated once and the dP accumulator is seeded with
 // Delta, so the product yields Delta - dP and dS costs one multiply (the sign is folded into
 // the final dK scale).
-template <int D, int BQ, bool MAPPED>
+template <int D, int BQ, int MODE>
 __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
+  constexpr bool MAPPED = MODE != 0;
   constexpr int BK = 128, NB = BQ / 32;
   using QT = Tile<BQ, D>;
   constexpr int NL = QT::LOADS;
@@ -701,10 +781,15 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
     int id[NL];
     if constexpr (MAPPED) ids_of<BQ, D>(idr[t & 3], ls, wave, id);
     load_ids(t + 1);
-    if constexpr (MAPPED)
+    if constexpr (MODE == 1) {
+      uint32_t o[Tile<BQ, D>::LOADS];
+      mapped_offsets<BQ, D>(id, hq.rsb, ls, o);
+      stage_mapped32<BQ, D>(hq, o, B1 ? qs1 : qs0, wave);
+    } else if constexpr (MODE == 2) {
       stage_mapped<BQ, D>(hq, ls, id, B1 ? qs1 : qs0, wave);
-    else
+    } else {
       stage_strided<BQ, D>(hq, ls, q0, S, B1 ? qs1 : qs0, wave);
+    }
     stage_strided<BQ, D>(hd, ls, q0, S, B1 ? ds1 : ds0, wave);
     if (wave == 0) stage_words(lb + q0, B1 ? ls1 : ls0, lane, BQ);
     if (wave == 1) stage_words(dlb + q0, B1 ? dl1 : dl0, lane, BQ);
@@ -1033,8 +1118,9 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
 // Workgroup = 128 queries (the forward's layout) over key tiles of BN: S^T = K Q^T and
 // dP^T = V dO^T (K and V rows staged), dS^T feeds dQ^T = K^T dS^T as the B operand, with K^T
 // read from the staged K rows by transposing reads.
-template <int D, int BN, bool MAPPED>
+template <int D, int BN, int MODE>
 __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
+  constexpr bool MAPPED = MODE != 0;
   constexpr int BM = 128, NBK = BN / 32;
   using KT = Tile<BN, D>;
   constexpr int NL = KT::LOADS;
@@ -1093,7 +1179,12 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
     int id[NL];
     if constexpr (MAPPED) ids_of<BN, D>(idr[t & 3], ls, wave, id);
     load_ids(t + 1);
-    if constexpr (MAPPED) {
+    if constexpr (MODE == 1) {
+      uint32_t o[Tile<BN, D>::LOADS];
+      mapped_offsets<BN, D>(id, hk.rsb, ls, o);
+      stage_mapped32<BN, D>(hk, o, B1 ? ks1 : ks0, wave);
+      stage_mapped32<BN, D>(hv, o, B1 ? vs1 : vs0, wave);
+    } else if constexpr (MODE == 2) {
       stage_mapped<BN, D>(hk, ls, id, B1 ? ks1 : ks0, wave);
       stage_mapped<BN, D>(hv, ls, id, B1 ? vs1 : vs0, wave);
     } else {
@@ -1188,25 +1279,29 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
 
 // Occupancy: at D = 64 both passes run two waves per SIMD; at D = 128 the query pass runs two
 // waves with 32-key tiles, the key pass one wave (its accumulators live in AGPRs).
-#define LH_KV(NAME, D, BQ, MAPPED, ATTR)                                  \
+#define LH_KV(NAME, D, BQ, MODE, ATTR)                                    \
   __global__ __launch_bounds__(256) ATTR void NAME(BwdArgs a) {           \
-    attn_bwd_kv_body<D, BQ, MAPPED>(a);                                   \
+    attn_bwd_kv_body<D, BQ, MODE>(a);                                     \
   }
-#define LH_Q(NAME, D, BN, MAPPED)                                                          \
+#define LH_Q(NAME, D, BN, MODE)                                                            \
   __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void NAME( \
       BwdArgs a) {                                                                         \
-    attn_bwd_q_body<D, BN, MAPPED>(a);                                                     \
+    attn_bwd_q_body<D, BN, MODE>(a);                                                       \
   }
 #define LH_TWO_WAVES __attribute__((amdgpu_waves_per_eu(2, 2)))
 #define LH_ONE_WAVE
-LH_KV(attn_bwd_kv_d64, 64, 64, false, LH_TWO_WAVES)
-LH_KV(attn_bwd_kv_d128, 128, 32, false, LH_ONE_WAVE)
-LH_KV(attn_bwd_kv_mapped_d64, 64, 64, true, LH_TWO_WAVES)
-LH_KV(attn_bwd_kv_mapped_d128, 128, 32, true, LH_ONE_WAVE)
-LH_Q(attn_bwd_q_d64, 64, 64, false)
-LH_Q(attn_bwd_q_d128, 128, 32, false)
-LH_Q(attn_bwd_q_mapped_d64, 64, 64, true)
-LH_Q(attn_bwd_q_mapped_d128, 128, 32, true)
+LH_KV(attn_bwd_kv_d64, 64, 64, 0, LH_TWO_WAVES)
+LH_KV(attn_bwd_kv_d128, 128, 32, 0, LH_ONE_WAVE)
+LH_KV(attn_bwd_kv_mapped_d64, 64, 64, 1, LH_TWO_WAVES)
+LH_KV(attn_bwd_kv_mapped_d128, 128, 32, 1, LH_ONE_WAVE)
+LH_KV(attn_bwd_kv_mapped64_d64, 64, 64, 2, LH_TWO_WAVES)
+LH_KV(attn_bwd_kv_mapped64_d128, 128, 32, 2, LH_ONE_WAVE)
+LH_Q(attn_bwd_q_d64, 64, 64, 0)
+LH_Q(attn_bwd_q_d128, 128, 32, 0)
+LH_Q(attn_bwd_q_mapped_d64, 64, 64, 1)
+LH_Q(attn_bwd_q_mapped_d128, 128, 32, 1)
+LH_Q(attn_bwd_q_mapped64_d64, 64, 64, 2)
+LH_Q(attn_bwd_q_mapped64_d128, 128, 32, 2)
 #undef LH_KV
 #undef LH_Q
 #undef LH_TWO_WAVES
@@ -1276,6 +1371,15 @@ RowSrc mapped_rows(const Levels& lv, const void* x, const void* px) {
 }  // namespace
 
 // ------------------------------------------------------------------------ launchers
+// Mapped calls use 32-bit row offsets when every pyramid row of a head (N + P1 rows of
+// H * D bf16) lies within 4 GiB of the head's first raw row.
+int mapped_mode(const AttnCall& c) {
+  if (!c.mapped) return 0;
+  const int64_t rows = c.lv->N + c.lv->P1;
+  const int64_t rsb = static_cast<int64_t>(c.lv->H) * c.lv->D * 2;
+  return rows * rsb < (int64_t(1) << 32) ? 1 : 2;
+}
+
 hipError_t launch_attn_fwd2(const AttnCall& c, const void* q, const void* k, const void* v,
                             float* o, float* lse, hipStream_t st) {
   FwdArgs a;
@@ -1302,12 +1406,10 @@ hipError_t launch_attn_fwd2(const AttnCall& c, const void* q, const void* k, con
   a.causal = c.causal;
   a.sl2 = c.scale * kLog2e;
   const unsigned blocks = static_cast<unsigned>(a.BH * (a.Sp / 128));
-  if (c.D == 64)
-    hipLaunchKernelGGL(c.mapped ? attn_fwd_mapped_d64 : attn_fwd_d64, dim3(blocks), dim3(256), 0,
-                       st, a);
-  else
-    hipLaunchKernelGGL(c.mapped ? attn_fwd_mapped_d128 : attn_fwd_d128, dim3(blocks), dim3(256),
-                       0, st, a);
+  static void (*const kern[2][3])(FwdArgs) = {
+      {attn_fwd_d64, attn_fwd_mapped_d64, attn_fwd_mapped64_d64},
+      {attn_fwd_d128, attn_fwd_mapped_d128, attn_fwd_mapped64_d128}};
+  hipLaunchKernelGGL(kern[c.D == 64 ? 0 : 1][mapped_mode(c)], dim3(blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1346,24 +1448,19 @@ hipError_t launch_attn_bwd2(int pass, const AttnCall& c, const void* q, const vo
   a.scale = c.scale;
   a.sl2 = c.scale * kLog2e;
   const unsigned blocks = static_cast<unsigned>(a.BH * (a.Sp / 128));
+  const int di = c.D == 64 ? 0 : 1, m = mapped_mode(c);
+  static void (*const kv[2][3])(BwdArgs) = {
+      {attn_bwd_kv_d64, attn_bwd_kv_mapped_d64, attn_bwd_kv_mapped64_d64},
+      {attn_bwd_kv_d128, attn_bwd_kv_mapped_d128, attn_bwd_kv_mapped64_d128}};
+  static void (*const qp[2][3])(BwdArgs) = {
+      {attn_bwd_q_d64, attn_bwd_q_mapped_d64, attn_bwd_q_mapped64_d64},
+      {attn_bwd_q_d128, attn_bwd_q_mapped_d128, attn_bwd_q_mapped64_d128}};
   if (pass & 1) {
-    if (c.D == 64)
-      hipLaunchKernelGGL(c.mapped ? attn_bwd_kv_mapped_d64 : attn_bwd_kv_d64, dim3(blocks),
-                         dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(c.mapped ? attn_bwd_kv_mapped_d128 : attn_bwd_kv_d128, dim3(blocks),
-                         dim3(256), 0, st, a);
+    hipLaunchKernelGGL(kv[di][m], dim3(blocks), dim3(256), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (pass & 2) {
-    if (c.D == 64)
-      hipLaunchKernelGGL(c.mapped ? attn_bwd_q_mapped_d64 : attn_bwd_q_d64, dim3(blocks),
-                         dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(c.mapped ? attn_bwd_q_mapped_d128 : attn_bwd_q_d128, dim3(blocks),
-                         dim3(256), 0, st, a);
-  }
+  if (pass & 2) hipLaunchKernelGGL(qp[di][m], dim3(blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
