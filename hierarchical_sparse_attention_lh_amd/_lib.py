@@ -78,6 +78,7 @@ _SIGS = {
     "lh_status_string": [ctypes.c_int],
     "lh_pool_score": [_CFG, P, P, P, P, P, P, _I32, P, P],
     "lh_topk": [_CFG, P, P, P],
+    "lh_pool_score_topk": [_CFG, P, P, P, P, P, P, _I32, P, P, P],
     "lh_build_map": [_CFG, P, P, P, P],
     "lh_gather": [_CFG, P, P, P, P, P, P, _I32, P, P, P, P, P, P, P],
     "lh_attn_fwd": [_DESC, P, P, P, P, P, P],

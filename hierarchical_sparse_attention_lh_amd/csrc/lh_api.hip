@@ -350,6 +350,20 @@ lh_status lh_topk(const lh_config* cfg, const float* scores, int32_t* sel, lh_st
   return launched(lh::launch_topk(L, scores, sel, st), st);
 }
 
+lh_status lh_pool_score_topk(const lh_config* cfg, const void* q, const void* k, const void* v,
+                             void* pq, void* pk, void* pv, int32_t pooled_dtype, float* scores,
+                             int32_t* sel, lh_stream_t stream) {
+  Levels L;
+  LH_TRY(check_config(cfg, &L));
+  LH_TRY(need(q)); LH_TRY(need(k)); LH_TRY(need(v)); LH_TRY(need(scores));
+  LH_TRY(maybe(pq)); LH_TRY(maybe(pk)); LH_TRY(maybe(pv));
+  if (L.K > 0) LH_TRY(need(sel));
+  if (pooled_dtype != LH_BF16 && pooled_dtype != LH_F32) return LH_ERR_DTYPE;
+  auto st = static_cast<hipStream_t>(stream);
+  return launched(lh::launch_pool_score_topk(L, cfg->dtype == LH_F32, q, k, v, pq, pk, pv,
+                                             pooled_dtype == LH_F32, scores, sel, st), st);
+}
+
 lh_status lh_build_map(const lh_config* cfg, const int32_t* sel, int32_t* gmap, int32_t* inv,
                        lh_stream_t stream) {
   Levels L;
@@ -499,6 +513,9 @@ lh_status forward_body(const lh_config* cfg, const Levels& L, const lh_plan_info
   float* og = reinterpret_cast<float*>(at(saved, P.saved_o));
   float* lse = reinterpret_cast<float*>(at(saved, P.saved_lse));
 
+  // separate pooling and top-K launches: on MI355X they beat the fused pass of
+  // lh_pool_score_topk (the pooling is HBM-bound either way; inside the fused workgroups the
+  // top-K phase leaves the memory pipe idle)
   LH_TRY(launched(lh::launch_pool_score(L, f32, q, k, v, pq, pk, pv, 0, scores, st), st));
   LH_TRY(launched(lh::launch_topk(L, scores, sel, st), st));
   LH_TRY(launched(lh::launch_build_map(L, sel, gmap, inv, st), st));

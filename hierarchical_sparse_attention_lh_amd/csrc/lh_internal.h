@@ -86,6 +86,15 @@ hipError_t launch_pool_score(const Levels& lv, int32_t in_f32, const void* q, co
                              const void* v, void* pq, void* pk, void* pv, int32_t out_f32,
                              float* scores, hipStream_t st);
 hipError_t launch_topk(const Levels& lv, const float* scores, int32_t* sel, hipStream_t st);
+// Top-K of the chunks of levels first..last only.
+hipError_t launch_topk_levels(const Levels& lv, int first, int last, const float* scores,
+                              int32_t* sel, hipStream_t st);
+// Pooling, scoring and top-K in one pass where the finest selected level's chunks cover whole
+// coarsest blocks (its scores then stay in LDS and are not written to `scores`); otherwise
+// launch_pool_score followed by launch_topk.
+hipError_t launch_pool_score_topk(const Levels& lv, int32_t in_f32, const void* q,
+                                  const void* k, const void* v, void* pq, void* pk, void* pv,
+                                  int32_t out_f32, float* scores, int32_t* sel, hipStream_t st);
 hipError_t launch_build_map(const Levels& lv, const int32_t* sel, int32_t* gmap, int32_t* inv,
                             hipStream_t st);
 // Gathered rows [B, H, Sp, D] bf16 of q/k/v (level 0) or the pooled levels (gmap ids).

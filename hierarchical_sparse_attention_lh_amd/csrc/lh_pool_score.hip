@@ -16,6 +16,9 @@
 // A wave reads 64 x 16 B = 1 KB of one token row per step: fully coalesced.  Q, K and V are
 // separate grid rows (blockIdx.y) so the three streams run concurrently.  Under the DIRECT
 // selection reading the raw key rows (level 0) are scored as well.
+#include <type_traits>
+
+#include "lh_chunk_topk.h"
 #include "lh_internal.h"
 
 namespace lh {
@@ -63,6 +66,9 @@ struct Ctx {
   int hd8;         // D / 8 lanes per head
   bool writer;     // first lane of the head
   bool score0;     // also score the raw tokens (level 0; DIRECT selection reads them)
+  int lds_level;   // scores of this level go to `lds` (entry j at lds[j - lds_base]); -1: none
+  int64_t lds_base;
+  float* lds;
 };
 
 // l2 norm of entry (level, j) of this head: the thread's 8 squares in float64, reduced over
@@ -74,7 +80,12 @@ __device__ __forceinline__ void score(const Ctx<Tin, Tout>& c, const Levels& lv,
 #pragma unroll
   for (int i = 0; i < 8; ++i) ss += static_cast<double>(v[i]) * static_cast<double>(v[i]);
   for (int m = 1; m < c.hd8; m <<= 1) ss += __shfl_xor(ss, m);
-  if (c.writer) c.sc[lv.off[level] + j] = static_cast<float>(sqrt(ss));
+  if (c.writer) {
+    if (level == c.lds_level)
+      c.lds[j - c.lds_base] = static_cast<float>(sqrt(ss));
+    else
+      c.sc[lv.off[level] + j] = static_cast<float>(sqrt(ss));
+  }
 }
 
 template <typename Tin, typename Tout>
@@ -197,6 +208,9 @@ __global__ __launch_bounds__(256) void pool_score_kernel(Levels lv, const Tin* _
   c.hd8 = hd8;
   c.writer = (g % hd8) == 0;
   c.score0 = stream == 1 && lv.direct;
+  c.lds_level = -1;
+  c.lds_base = 0;
+  c.lds = nullptr;
 
   float out[8];
   pool_block<L - 1>(c, lv, tile * T, out);
@@ -219,7 +233,10 @@ struct Ctx3 {
   int hd8;
   bool writer;
   bool score0;
-  int scorer;       // 1 = qk, 2 = qkv
+  int scorer;       // 0 = k, 1 = qk, 2 = qkv
+  int lds_level;    // scores of this level go to `lds` (entry j at lds[j - lds_base]); -1: none
+  int64_t lds_base;
+  float* lds;
 };
 
 __device__ __forceinline__ double lane_ssq(const float (&v)[8], int hd8) {
@@ -234,16 +251,21 @@ template <typename Tin, typename Tout>
 __device__ __forceinline__ void score3(const Ctx3<Tin, Tout>& c, const Levels& lv, int level,
                                        int64_t j, const float (&vq)[8], const float (&vk)[8],
                                        const float (&vv)[8]) {
-  const double sq = lane_ssq(vq, c.hd8);
   const double sk = lane_ssq(vk, c.hd8);
   double s;
-  if (c.scorer == 1) {
-    s = sqrt(sq) * sqrt(sk);
+  if (c.scorer == 0) {
+    s = sqrt(sk);
+  } else if (c.scorer == 1) {
+    s = sqrt(lane_ssq(vq, c.hd8)) * sqrt(sk);
   } else {
-    const double sv = lane_ssq(vv, c.hd8);
-    s = sqrt(sq + sk + sv);
+    s = sqrt(lane_ssq(vq, c.hd8) + sk + lane_ssq(vv, c.hd8));
   }
-  if (c.writer) c.sc[lv.off[level] + j] = static_cast<float>(s);
+  if (c.writer) {
+    if (level == c.lds_level)
+      c.lds[j - c.lds_base] = static_cast<float>(s);
+    else
+      c.sc[lv.off[level] + j] = static_cast<float>(s);
+  }
 }
 
 template <typename Tin, typename Tout>
@@ -351,9 +373,100 @@ __global__ __launch_bounds__(256) void pool_score3_kernel(Levels lv, int scorer,
   c.writer = (g % hd8) == 0;
   c.score0 = lv.direct;
   c.scorer = scorer;
+  c.lds_level = -1;
+  c.lds_base = 0;
+  c.lds = nullptr;
 
   float out[3][8];
   pool_block3<L - 1>(c, lv, tile * T, out);
+}
+
+// ------------------------------------------------------ fused pool + score + top-K
+// One workgroup per (batch, head, chunk c of the finest selected level f): it pools Q, K and
+// V of the chunk's token span (W p^f tokens, a whole number of coarsest blocks), writes the
+// pooled rows and the scores of the other levels, keeps level f's W scores in LDS and runs
+// the chunk's bitonic top-K in place -- the scores of that level never leave the workgroup.
+// The chunks of coarser levels span several workgroups; lh_topk's kernel selects those
+// afterwards.  Threads: D/8 lanes per 16-byte column group of the head, 256 / (D/8)
+// "walkers" taking the span's coarsest blocks in turn.
+template <int L, bool SPLIT, typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void pool_score_topk_kernel(Levels lv, int scorer,
+                                                              const Tin* __restrict__ q,
+                                                              const Tin* __restrict__ k,
+                                                              const Tin* __restrict__ v,
+                                                              Tout* pq, Tout* pk, Tout* pv,
+                                                              float* scores, int32_t* sel) {
+  __shared__ float fsc[kTopkMaxWidth];
+  __shared__ uint64_t key[kTopkMaxWidth];
+  __shared__ int32_t flag[kTopkMaxWidth];
+  __shared__ int32_t part[kTopkThreads];
+  const int f = lv.sel_first;
+  const int64_t ch = blockIdx.x;
+  const int64_t bh = blockIdx.y, b = bh / lv.H, h = bh % lv.H;
+  const int W = static_cast<int>(lv.width[f]);
+  const int64_t T = lv.pw[L - 1];
+  const int64_t span = W * lv.pw[f];
+  const int64_t t0 = ch * span, nblk = span / T;
+  const int hd8 = lv.D / 8;
+  const int g = threadIdx.x % hd8, walker = threadIdx.x / hd8, walkers = 256 / hd8;
+  const int64_t row = static_cast<int64_t>(lv.H) * lv.D;
+  const int64_t col = h * lv.D + g * 8;
+
+  if constexpr (SPLIT) {
+    // key scorer: (stream, block) items, one stream per item as in pool_score_kernel
+    Ctx<Tin, Tout> c;
+    c.row = row;
+    c.p = lv.p;
+    c.inv_p = 1.0f / static_cast<float>(lv.p);
+    c.hd8 = hd8;
+    c.writer = g == 0;
+    c.lds_level = f;
+    c.lds_base = ch * W;
+    c.lds = fsc;
+    for (int64_t it = walker; it < 3 * nblk; it += walkers) {
+      const int stream = static_cast<int>(it / nblk);
+      const int64_t blk = it % nblk;
+      const Tin* x = stream == 0 ? q : (stream == 1 ? k : v);
+      Tout* px = stream == 0 ? pq : (stream == 1 ? pk : pv);
+      if (px == nullptr && stream != 1) continue;
+      c.x = x + b * lv.N * row + col;
+      c.px = px ? px + b * lv.P1 * row + col : nullptr;
+      c.sc = stream == 1 ? scores + bh * lv.P : nullptr;
+      c.score0 = stream == 1 && lv.direct;
+      float out[8];
+      pool_block<L - 1>(c, lv, t0 + blk * T, out);
+    }
+  } else {
+    Ctx3<Tin, Tout> c;
+    c.row = row;
+    const Tin* xs[3] = {q, k, v};
+    Tout* ps[3] = {pq, pk, pv};
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      c.x[s] = xs[s] + b * lv.N * row + col;
+      c.px[s] = ps[s] ? ps[s] + b * lv.P1 * row + col : nullptr;
+    }
+    c.sc = scores + bh * lv.P;
+    c.p = lv.p;
+    c.inv_p = 1.0f / static_cast<float>(lv.p);
+    c.hd8 = hd8;
+    c.writer = g == 0;
+    c.score0 = lv.direct;
+    c.scorer = scorer;
+    c.lds_level = f;
+    c.lds_base = ch * W;
+    c.lds = fsc;
+    for (int64_t blk = walker; blk < nblk; blk += walkers) {
+      float out[3][8];
+      pool_block3<L - 1>(c, lv, t0 + blk * T, out);
+    }
+  }
+  __syncthreads();
+  const int64_t nch = lv.nchunk[f];
+  const int64_t base = lv.keff[f] / nch, rem = lv.keff[f] % nch;
+  const int quota = static_cast<int>(base + (ch < rem ? 1 : 0));
+  const int64_t first_out = ch * base + (ch < rem ? ch : rem);
+  chunk_topk(fsc, W, quota, ch * W, sel + bh * lv.K + lv.soff[f] + first_out, key, flag, part);
 }
 
 template <typename Tin, typename Tout>
@@ -404,7 +517,64 @@ hipError_t dispatch(const Levels& lv, const void* q, const void* k, const void* 
   return hipGetLastError();
 }
 
+bool pool_topk_fusable(const Levels& lv) {
+  if (lv.L < 2 || lv.K == 0 || lv.sel_first > lv.sel_last) return false;
+  const int f = lv.sel_first;
+  const int64_t span = lv.width[f] * lv.pw[f];
+  return span % lv.pw[lv.L - 1] == 0 && lv.width[f] <= kTopkMaxWidth;
+}
+
+template <typename Tin, typename Tout>
+hipError_t dispatch_fused(const Levels& lv, const void* q, const void* k, const void* v,
+                          void* pq, void* pk, void* pv, float* scores, int32_t* sel,
+                          hipStream_t st) {
+  dim3 grid(static_cast<unsigned>(lv.nchunk[lv.sel_first]), static_cast<unsigned>(lv.B * lv.H));
+  const int sc = lv.scorer == LH_SCORE_K ? 0 : (lv.scorer == LH_SCORE_QK ? 1 : 2);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, lv, sc, static_cast<const Tin*>(q),
+                       static_cast<const Tin*>(k), static_cast<const Tin*>(v),
+                       static_cast<Tout*>(pq), static_cast<Tout*>(pk), static_cast<Tout*>(pv),
+                       scores, sel);
+  };
+  auto by_levels = [&](auto split) {
+    constexpr bool S = decltype(split)::value;
+    switch (lv.L) {
+      case 2: go(pool_score_topk_kernel<2, S, Tin, Tout>); break;
+      case 3: go(pool_score_topk_kernel<3, S, Tin, Tout>); break;
+      case 4: go(pool_score_topk_kernel<4, S, Tin, Tout>); break;
+      case 5: go(pool_score_topk_kernel<5, S, Tin, Tout>); break;
+      case 6: go(pool_score_topk_kernel<6, S, Tin, Tout>); break;
+      case 7: go(pool_score_topk_kernel<7, S, Tin, Tout>); break;
+      default: go(pool_score_topk_kernel<8, S, Tin, Tout>); break;
+    }
+  };
+  if (sc == 0)
+    by_levels(std::true_type{});
+  else
+    by_levels(std::false_type{});
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_pool_score_topk(const Levels& lv, int32_t in_f32, const void* q, const void* k,
+                                  const void* v, void* pq, void* pk, void* pv, int32_t out_f32,
+                                  float* scores, int32_t* sel, hipStream_t st) {
+  if (!pool_topk_fusable(lv)) {  // separate passes
+    hipError_t e = launch_pool_score(lv, in_f32, q, k, v, pq, pk, pv, out_f32, scores, st);
+    if (e != hipSuccess) return e;
+    return launch_topk(lv, scores, sel, st);
+  }
+  hipError_t e;
+  if (in_f32)
+    e = out_f32 ? dispatch_fused<float, float>(lv, q, k, v, pq, pk, pv, scores, sel, st)
+                : dispatch_fused<float, uint16_t>(lv, q, k, v, pq, pk, pv, scores, sel, st);
+  else
+    e = out_f32 ? dispatch_fused<uint16_t, float>(lv, q, k, v, pq, pk, pv, scores, sel, st)
+                : dispatch_fused<uint16_t, uint16_t>(lv, q, k, v, pq, pk, pv, scores, sel, st);
+  if (e != hipSuccess) return e;
+  return launch_topk_levels(lv, lv.sel_first + 1, lv.sel_last, scores, sel, st);
+}
 
 hipError_t launch_pool_score(const Levels& lv, int32_t in_f32, const void* q, const void* k,
                              const void* v, void* pq, void* pk, void* pv, int32_t out_f32,

@@ -97,6 +97,24 @@ def lh_topk(cfg, scores):
     return sel
 
 
+def lh_pool_score_topk(cfg, q, k, v, pooled_dtype=torch.float32):
+    """Stages 1-3 in one call: returns (pq, pk, pv, scores, sel).  When the fused kernel runs,
+    the scores of the finest selected level are left as NaN (never written)."""
+    _check_tokens(cfg, q, k, v)
+    info = lh_plan(cfg)
+    dev = q.device
+    shape = (cfg.batch, max(1, info.pooled_rows), cfg.heads, cfg.head_dim)
+    pq, pk, pv = (torch.empty(shape, dtype=pooled_dtype, device=dev) for _ in range(3))
+    scores = torch.full((cfg.batch, cfg.heads, info.pyramid_total), float("nan"),
+                        dtype=torch.float32, device=dev)
+    sel = torch.empty((cfg.batch, cfg.heads, max(1, info.sel_total)), dtype=torch.int32,
+                      device=dev)
+    code = LH_F32 if pooled_dtype == torch.float32 else LH_BF16
+    check(_lib.load().lh_pool_score_topk(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(pq),
+                                         _p(pk), _p(pv), code, _p(scores), _p(sel), _stream()))
+    return pq, pk, pv, scores, sel
+
+
 def lh_build_map(cfg, sel):
     info = lh_plan(cfg)
     dev = sel.device

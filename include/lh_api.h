@@ -186,6 +186,19 @@ lh_status lh_pool_score(const lh_config* cfg, const void* q, const void* k, cons
  *          at sel_offset[l] .. sel_offset[l] + k_eff[l] - 1 */
 lh_status lh_topk(const lh_config* cfg, const float* scores, int32_t* sel, lh_stream_t stream);
 
+/* Stages 1-3 as one call ([WS] item 1 and item 2): the pooled rows of lh_pool_score and the
+ * selection of lh_topk, identical to calling the two in turn.  Where a chunk of the finest
+ * selected level f covers a whole number of coarsest blocks (C p^f a multiple of p^(L-1)),
+ * one workgroup per chunk pools its token span, keeps level f's scores on chip and selects
+ * that chunk in place; scores[.., level f] are then NOT written (every other level's are),
+ * and the coarser selected levels follow in a second launch.  Otherwise the two stages run
+ * as separate launches and every score is written.  Arguments as in lh_pool_score and
+ * lh_topk; sel may be NULL only when sel_total is 0.  (lh_forward runs the two stages as
+ * separate launches, which measure faster on MI355X: the pooling is HBM-bound either way.) */
+lh_status lh_pool_score_topk(const lh_config* cfg, const void* q, const void* k, const void* v,
+                             void* pq, void* pk, void* pv, int32_t pooled_dtype, float* scores,
+                             int32_t* sel, lh_stream_t stream);
+
 /* Stage 4a ([EN] four-stage, [WS] item 3): the gathered order.
  *   sel  device int32 [B, H, sel_total] from lh_topk
  *   gmap device int32 [B, H, Sp]: pyramid id of each gathered slot, in (e, l) order;

@@ -114,7 +114,11 @@ def test_full_size_selection_and_map_every_head(name):
     _, _, _, sc = ops.lh_pool_score(cfg, t["q"], t["k"], t["v"], pooled_dtype=torch.bfloat16)
     sel = ops.lh_topk(cfg, sc)
     gmap, inv = ops.lh_build_map(cfg, sel)
+    # the fused pool + score + top-K pass the layer runs keeps the same entries
+    _, _, _, _, fsel = ops.lh_pool_score_topk(cfg, t["q"], t["k"], t["v"],
+                                              pooled_dtype=torch.bfloat16)
     torch.cuda.synchronize()
+    assert torch.equal(sel, fsel)
     sel_np, gmap_np, inv_np = sel.cpu().numpy(), gmap.cpu().numpy(), inv.cpu().numpy()
     direct = w.mode == "direct"
     ocfg = O.Config(w.levels, w.pool, w.k, w.chunk, mode=O.DIRECT if direct else O.REFINE)

@@ -190,6 +190,86 @@ def test_topk_against_float64_scores_with_near_ties(w):
     print(f"[{w.name}] forgiven near-tie swaps: {swaps}")
 
 
+# ------------------------------------------------------------------------ stages 1-3 fused
+def _fusable(w, info):
+    """The fused pool + score + top-K kernel runs when a chunk of the finest selected level
+    covers a whole number of coarsest blocks."""
+    f = min(sel_levels(w), default=None)
+    if w.levels < 2 or info.sel_total == 0 or f is None:
+        return False
+    return info.chunk_width[f] * w.pool ** f % w.pool ** (w.levels - 1) == 0
+
+
+# a 512K-shaped selection (L = 4, p = 4, C = 1024: a level-1 chunk spans 4096 tokens) at 32K
+FUSED_C1024 = synth.Workload("fused-c1024", 1, 32768, 4, 64, "bf16", 4, 4, 700, 1024, 23, False)
+# DIRECT, C = 2048 over raw tokens (R = 8 keys per thread), D = 128, batch 2
+FUSED_DIRECT_C2048 = synth.Workload("fused-direct-c2048-d128", 2, 16384, 2, 128, "bf16", 3, 4,
+                                    1500, 2048, 24, False, "direct")
+# DIRECT with chunks narrower than a coarsest block: separate launches
+SPLIT_DIRECT = synth.Workload("split-direct", 1, 4096, 2, 64, "bf16", 4, 4, 20, 16, 25, False,
+                              "direct")
+FUSED_CASES = STAGE_CASES + [MEDIUM, FUSED_C1024, FUSED_DIRECT_C2048, SPLIT_DIRECT]
+
+
+def _check_fused(w, t, info, cfg):
+    pq, pk, pv, sc = ops.lh_pool_score(cfg, t["q"], t["k"], t["v"], pooled_dtype=torch.bfloat16)
+    sel = ops.lh_topk(cfg, sc)
+    fq, fk, fv, fsc, fsel = ops.lh_pool_score_topk(cfg, t["q"], t["k"], t["v"],
+                                                   pooled_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for a, b in ((pq, fq), (pk, fk), (pv, fv)):
+        assert torch.equal(a, b)
+    if info.sel_total:
+        assert torch.equal(sel[..., :info.sel_total], fsel[..., :info.sel_total])
+    fused = _fusable(w, info)
+    first = 0 if w.mode == "direct" else 1
+    for lv in range(first, w.levels):
+        o, n = info.level_offset[lv], info.level_size[lv]
+        if fused and lv == min(sel_levels(w)):  # kept on chip: never written
+            assert torch.isnan(fsc[:, :, o:o + n]).all(), lv
+        else:
+            assert torch.equal(sc[:, :, o:o + n], fsc[:, :, o:o + n]), lv
+    return fused
+
+
+@pytest.mark.parametrize("w", FUSED_CASES, ids=lambda w: w.name)
+def test_pool_score_topk_matches_separate_stages(w):
+    """One fused pass gives the pooled rows and the selection of lh_pool_score + lh_topk bit
+    for bit (the separate stages are checked against the oracle above)."""
+    t, _ = inputs(w, with_grad=False)
+    cfg = ops.config_for(w)
+    info = ops.lh_plan(cfg)
+    fused = _check_fused(w, t, info, cfg)
+    print(f"[{w.name}] fused kernel: {fused}")
+    if w in (FUSED_C1024, FUSED_DIRECT_C2048):
+        assert fused
+    if w is SPLIT_DIRECT:
+        assert not fused
+
+
+def test_pool_score_topk_exact_ties():
+    """Whole runs of equal scores inside every chunk (key tokens repeated in blocks of 64, so
+    16 consecutive level-1 and 4 consecutive level-2 entries tie exactly): both paths must keep
+    the lower indices."""
+    w = FUSED_C1024
+    t, _ = inputs(w, with_grad=False)
+    n = w.n_tokens
+    idx = torch.arange(n, device=DEV) // 64 * 64
+    t["k"] = t["k"][:, idx].contiguous()
+    cfg = ops.config_for(w)
+    info = ops.lh_plan(cfg)
+    assert _check_fused(w, t, info, cfg)
+    _, _, _, sc = ops.lh_pool_score(cfg, t["q"], t["k"], t["v"], pooled_dtype=torch.bfloat16)
+    sel = ops.lh_topk(cfg, sc).cpu().numpy()
+    sc_np = f64(sc)
+    for h in range(w.heads):
+        for lv in sel_levels(w):
+            o = info.level_offset[lv]
+            want = O.select_level(sc_np[0, h, o:o + info.level_size[lv]], w.k, w.chunk)
+            got = sel[0, h, info.sel_offset[lv]:info.sel_offset[lv] + info.k_eff[lv]]
+            assert np.array_equal(got, want), (h, lv)
+
+
 # ------------------------------------------------------------------------ stage 4
 @pytest.mark.parametrize("w", STAGE_CASES + [MEDIUM], ids=lambda w: w.name)
 def test_map_and_gather(w):
