@@ -1153,7 +1153,9 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       qreg[kk] = ld_op16(qr + 16 * kk + hl * 8);
-      oreg[kk] = ld_op16(dr + 16 * kk + hl * 8);
+      // dO negated (sign bits flipped), so the dP^T product seeded with Delta yields Delta - dP
+      const u32x4 u = *reinterpret_cast<const u32x4*>(dr + 16 * kk + hl * 8);
+      oreg[kk] = as_bf16x8(u ^ 0x80008000u);
     }
   }
   const float l2 = a.lse[bh * Sp + myq];
@@ -1208,13 +1210,15 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
 #pragma unroll
     for (int b2 = 0; b2 < NBK; ++b2) {
       sacc[b2] = zero16();
-      pacc[b2] = zero16();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pacc[b2][r] = dlt;  // every C register is this lane's query
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         sacc[b2] = mfma32(lds_at(ksb, b2 * 64 * D + ko[kk]), qreg[kk], sacc[b2]);
         pacc[b2] = mfma32(lds_at(vsb, b2 * 64 * D + ko[kk]), oreg[kk], pacc[b2]);
       }
     }
+    // pacc = Delta - dP, so P * pacc = -dS: one multiply; the sign goes into the final scale
 #pragma unroll
     for (int b2 = 0; b2 < NBK; ++b2)
 #pragma unroll
@@ -1224,7 +1228,7 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
           const int key = k0 + b2 * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
           if ((causal && key > myq) || key >= S) p = 0.f;
         }
-        pacc[b2][r] = p * (pacc[b2][r] - dlt);
+        pacc[b2][r] = p * pacc[b2][r];
       }
 #pragma unroll
     for (int t4 = 0; t4 < 2 * NBK; ++t4) {
@@ -1265,12 +1269,13 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
   if (myq < a.g_rows) {
     float* dqr = a.dq + b * a.gsb + h * a.gsh + static_cast<int64_t>(myq) * a.gss;
     const bool live = myq < S;
+    const float nsc = -a.scale;  // dqacc holds -dQ^T / scale
 #pragma unroll
     for (int d2 = 0; d2 < D / 32; ++d2)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        float4 x = make_float4(dqacc[d2][4 * g] * a.scale, dqacc[d2][4 * g + 1] * a.scale,
-                               dqacc[d2][4 * g + 2] * a.scale, dqacc[d2][4 * g + 3] * a.scale);
+        float4 x = make_float4(dqacc[d2][4 * g] * nsc, dqacc[d2][4 * g + 1] * nsc,
+                               dqacc[d2][4 * g + 2] * nsc, dqacc[d2][4 * g + 3] * nsc);
         if (!live) x = make_float4(0.f, 0.f, 0.f, 0.f);
         *reinterpret_cast<float4*>(dqr + d2 * 32 + g * 8 + hl * 4) = x;
       }
