@@ -143,6 +143,9 @@ def test_entry_points_reject_bad_pointers_before_launch():
     assert _call("lh_pool_score", c, ok, bad, ok, ok, ok, ok, 0, ok, st) == L["LH_ERR_ALIGN"]
     assert _call("lh_pool_score", c, ok, ok, ok, ok, ok, ok, 5, ok, st) == L["LH_ERR_DTYPE"]
     assert _call("lh_topk", c, null, ok, st) == L["LH_ERR_NULL"]
+    assert _call("lh_pool_score_topk", c, ok, ok, ok, ok, ok, ok, 0, ok, null, st) == L["LH_ERR_NULL"]
+    assert _call("lh_pool_score_topk", c, ok, ok, ok, ok, ok, ok, 5, ok, ok, st) == L["LH_ERR_DTYPE"]
+    assert _call("lh_pool_score_topk", c, ok, ok, ok, null, ok, null, 0, bad, ok, st) == L["LH_ERR_ALIGN"]
     assert _call("lh_build_map", c, ok, bad, ok, st) == L["LH_ERR_ALIGN"]
     assert _call("lh_gather", c, ok, ok, ok, ok, ok, ok, 0, ok, ok, ok, ok, ok, null, st) == L["LH_ERR_NULL"]
     assert _call("lh_gather", c, ok, ok, ok, ok, ok, ok, 0, null, ok, ok, ok, ok, ok, st) == L["LH_ERR_NULL"]

@@ -247,6 +247,33 @@ def test_pool_score_topk_matches_separate_stages(w):
         assert not fused
 
 
+def test_pool_score_topk_without_pooled_outputs():
+    """Pooled outputs are optional: with pq and pv NULL (and pk NULL too) the fused pass keeps
+    the same entries, and the rows it was asked for are identical."""
+    import ctypes
+    from hierarchical_sparse_attention_lh_amd import _lib
+    for w in (FUSED_C1024, SCORER_QK):
+        t, _ = inputs(w, with_grad=False)
+        cfg = ops.config_for(w)
+        info = ops.lh_plan(cfg)
+        _, pk, _, _, sel = ops.lh_pool_score_topk(cfg, t["q"], t["k"], t["v"],
+                                                  pooled_dtype=torch.bfloat16)
+        for keep_k in (True, False):
+            pk2 = torch.zeros_like(pk) if keep_k else None
+            sc2 = torch.empty((w.batch, w.heads, info.pyramid_total), dtype=torch.float32,
+                              device=DEV)
+            sel2 = torch.empty_like(sel)
+            code = _lib.load().lh_pool_score_topk(
+                ctypes.byref(cfg), ops._p(t["q"]), ops._p(t["k"]), ops._p(t["v"]), None,
+                ops._p(pk2) if keep_k else None, None, _lib.LH_BF16, ops._p(sc2), ops._p(sel2),
+                ops._stream())
+            assert code == 0
+            torch.cuda.synchronize()
+            assert torch.equal(sel2[..., :info.sel_total], sel[..., :info.sel_total]), (w.name, keep_k)
+            if keep_k:
+                assert torch.equal(pk2, pk), w.name
+
+
 def test_pool_score_topk_exact_ties():
     """Whole runs of equal scores inside every chunk (key tokens repeated in blocks of 64, so
     16 consecutive level-1 and 4 consecutive level-2 entries tie exactly): both paths must keep
