@@ -159,3 +159,44 @@ def test_layer_at_abi_bounds(w):
         tol = 2e-2 + 2.0**-8 * np.abs(ref)
         print(f"[{w.name}] {name}: worst err/tol {(err / tol).max():.3f}")
         assert np.all(err <= tol), (name, float(err.max()))
+
+
+# ------------------------------------------------- mapped rows beyond a 32-bit offset
+# Mapped attention switches to 64-bit row addressing when a head's pyramid rows (N raw plus
+# P1 pooled rows of H * D bf16) span 4 GiB or more.  These shapes cross that line (L = 2,
+# p = 16, C = 1024: N + P1 = 539,648 rows of 8 KiB); the mapped kernels must then give exactly
+# what the strided kernels give on the gathered copy of the same rows.
+LARGE_ROWS = [(32, 128), (64, 64)]
+
+
+@pytest.mark.parametrize("heads,d", LARGE_ROWS, ids=lambda v: str(v))
+def test_mapped_attention_with_64bit_row_offsets(heads, d):
+    n, levels, pool, k, chunk = 507904, 2, 16, 1024, 1024
+    cfg = ops.make_config(1, n, heads, d, levels, pool, k, chunk)
+    info = ops.lh_plan(cfg)
+    assert (n + info.pooled_rows) * heads * d * 2 >= 1 << 32  # the 64-bit addressing path
+    print(f"[rows64] H={heads} D={d} S={info.gathered_len}", flush=True)
+    gen = torch.Generator(device=DEV).manual_seed(61 + d)
+    x = {nm: torch.randn((1, n, heads, d), generator=gen, device=DEV, dtype=torch.bfloat16)
+         for nm in ("q", "k", "v", "dy")}
+    pq, pk, pv, sc = ops.lh_pool_score(cfg, x["q"], x["k"], x["v"], pooled_dtype=torch.bfloat16)
+    sel = ops.lh_topk(cfg, sc)
+    del sc
+    gmap, inv, g = ops.lh_gather(cfg, x["q"], x["k"], x["v"], pq, pk, pv, sel)
+    S = info.gathered_len
+    og, lse = ops.lh_attn_fwd_mapped(cfg, x["q"], x["k"], x["v"], pq, pk, pv, gmap)
+    dog, delta = ops.lh_scatter_bwd(cfg, gmap, og, x["dy"])
+    del x["dy"]
+    dqg, dkg, dvg = ops.lh_attn_bwd_mapped(cfg, x["q"], x["k"], x["v"], pq, pk, pv, gmap, lse,
+                                           delta, dog)
+    rows = {nm: g[nm][:, :, :S] for nm in "qkv"}
+    o2, lse2 = ops.lh_attn_fwd(rows["q"], rows["k"], rows["v"])
+    torch.cuda.synchronize()
+    assert torch.equal(og[:, :, :S], o2) and torch.equal(lse[:, :, :S], lse2[:, :, :S])
+    dq2, dk2, dv2 = ops.lh_attn_bwd(rows["q"], rows["k"], rows["v"], og[:, :, :S], lse,
+                                    dog[:, :, :S])
+    torch.cuda.synchronize()
+    for a, b in ((dqg, dq2), (dkg, dk2), (dvg, dv2)):
+        assert torch.equal(a[:, :, :S], b)
+    del x, pq, pk, pv, g, rows, og, o2, dqg, dkg, dvg, dq2, dk2, dv2
+    torch.cuda.empty_cache()
