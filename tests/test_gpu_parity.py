@@ -208,7 +208,12 @@ FUSED_DIRECT_C2048 = synth.Workload("fused-direct-c2048-d128", 2, 16384, 2, 128,
 # DIRECT with chunks narrower than a coarsest block: separate launches
 SPLIT_DIRECT = synth.Workload("split-direct", 1, 4096, 2, 64, "bf16", 4, 4, 20, 16, 25, False,
                               "direct")
-FUSED_CASES = STAGE_CASES + [MEDIUM, FUSED_C1024, FUSED_DIRECT_C2048, SPLIT_DIRECT]
+# p = 3 with one level-1 chunk of 1536 entries (not a power of two: a padded network), which
+# spans all 4608 tokens, a whole number of coarsest blocks
+FUSED_P3_ONE_CHUNK = synth.Workload("fused-p3-one-chunk", 1, 4608, 2, 64, "bf16", 3, 3, 100, 2048,
+                                    26, False)
+FUSED_CASES = STAGE_CASES + [MEDIUM, FUSED_C1024, FUSED_DIRECT_C2048, SPLIT_DIRECT,
+                             FUSED_P3_ONE_CHUNK]
 
 
 def _check_fused(w, t, info, cfg):
@@ -241,7 +246,7 @@ def test_pool_score_topk_matches_separate_stages(w):
     info = ops.lh_plan(cfg)
     fused = _check_fused(w, t, info, cfg)
     print(f"[{w.name}] fused kernel: {fused}")
-    if w in (FUSED_C1024, FUSED_DIRECT_C2048):
+    if w in (FUSED_C1024, FUSED_DIRECT_C2048, FUSED_P3_ONE_CHUNK):
         assert fused
     if w is SPLIT_DIRECT:
         assert not fused
