@@ -93,10 +93,13 @@ constexpr int kRun = 64;
 
 // OFFSET = 1: token t takes entry floor((t+1)/p^l) - 1 of level l (scatter); OFFSET = 0:
 // entry floor(t/p^l) at weight 1/p^l (gather+pool backward).
+// The lanes of one head (D/8 >= 8 consecutive lanes, q = 0.. within the group, first lane
+// hbase of the wave) walk the same tokens: each batch's slot ids are loaded once per group,
+// one id per lane, and spread to the group's lanes by shuffles.
 template <int L, int OFFSET, int KPRE, typename Tout>
 __device__ __forceinline__ void walk_tokens(const Levels& lv, const int32_t* __restrict__ iv,
                                             const float* __restrict__ rows, Tout* __restrict__ out,
-                                            int64_t row, int t0, int t1) {
+                                            int64_t row, int t0, int t1, int q, int hbase) {
   float c[L][8];
   int cj[L];
   float w[L];
@@ -108,21 +111,24 @@ __device__ __forceinline__ void walk_tokens(const Levels& lv, const int32_t* __r
   }
   for (int tb = t0; tb < t1; tb += 8) {
     const int tl = (tb + 8 < t1 ? tb + 8 : t1) - 1;  // last token of the batch
-    int32_t s0[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) s0[u] = tb + u <= tl ? iv[tb + u] : -1;
-    int32_t pre[L][KPRE];
+    const int32_t mine = (q < 8 && tb + q <= tl) ? iv[tb + q] : -1;
+    int32_t mp[L];
     int jf[L];
 #pragma unroll
     for (int l = 1; l < L; ++l) {
       jf[l] = level_div(lv, l, tb + OFFSET) - OFFSET;
       const int jl = level_div(lv, l, tl + OFFSET) - OFFSET;
-#pragma unroll
-      for (int i = 0; i < KPRE; ++i) {
-        const int j = jf[l] + i;
-        pre[l][i] = (j >= 0 && j <= jl && j != cj[l]) ? iv[lv.off[l] + j] : -1;
-      }
+      const int j = jf[l] + q;
+      mp[l] = (q < KPRE && j >= 0 && j <= jl && j != cj[l]) ? iv[lv.off[l] + j] : -1;
     }
+    int32_t s0[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s0[u] = __shfl(mine, hbase + u);
+    int32_t pre[L][KPRE];
+#pragma unroll
+    for (int l = 1; l < L; ++l)
+#pragma unroll
+      for (int i = 0; i < KPRE; ++i) pre[l][i] = __shfl(mp[l], hbase + i);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int t = tb + u;
@@ -173,9 +179,10 @@ __global__ __launch_bounds__(256) void scatter_kernel(Levels lv, int64_t Sp,
   const int64_t t0 = (rr % runs) * kRun;
   const int64_t t1 = t0 + kRun < lv.N ? t0 + kRun : lv.N;
   const int64_t bh = b * lv.H + g / hd8;
-  walk_tokens<L, 1, KPRE>(lv, inv + bh * lv.P, og + bh * Sp * lv.D + (g % hd8) * 8,
-                    y + b * lv.N * G * 8 + g * 8, G * 8, static_cast<int>(t0),
-                    static_cast<int>(t1));
+  const int q = static_cast<int>(g % hd8);
+  walk_tokens<L, 1, KPRE>(lv, inv + bh * lv.P, og + bh * Sp * lv.D + q * 8,
+                          y + b * lv.N * G * 8 + g * 8, G * 8, static_cast<int>(t0),
+                          static_cast<int>(t1), q, static_cast<int>(threadIdx.x & 63) - q);
 }
 
 // -------------------------------------------------------------------- scatter backward
@@ -262,9 +269,10 @@ __global__ __launch_bounds__(256) void gather_pool_bwd_kernel(
   const int64_t t0 = (rr % runs) * kRun;
   const int64_t t1 = t0 + kRun < lv.N ? t0 + kRun : lv.N;
   const int64_t bh = b * lv.H + g / hd8;
-  walk_tokens<L, 0, KPRE>(lv, inv + bh * lv.P, gx + bh * Sp * lv.D + (g % hd8) * 8,
-                    dx + b * lv.N * G * 8 + g * 8, G * 8, static_cast<int>(t0),
-                    static_cast<int>(t1));
+  const int q = static_cast<int>(g % hd8);
+  walk_tokens<L, 0, KPRE>(lv, inv + bh * lv.P, gx + bh * Sp * lv.D + q * 8,
+                          dx + b * lv.N * G * 8 + g * 8, G * 8, static_cast<int>(t0),
+                          static_cast<int>(t1), q, static_cast<int>(threadIdx.x & 63) - q);
 }
 
 template <typename Tout>
