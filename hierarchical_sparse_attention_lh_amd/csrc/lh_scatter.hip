@@ -42,11 +42,6 @@ __device__ __forceinline__ void ld8(const uint16_t* p, float (&o)[8]) {
   }
 }
 
-__device__ __forceinline__ void st8(float* p, const float (&v)[8]) {
-  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
-}
-
 __device__ __forceinline__ void st8(uint16_t* p, const float (&v)[8]) {
   uint4 u;
   u.x = pack_bf16x2(v[0], v[1]);
@@ -74,8 +69,6 @@ __device__ __forceinline__ void st8_nt(uint16_t* p, const float (&v)[8]) {
   u.w = pack_bf16x2(v[6], v[7]);
   __builtin_nontemporal_store(u, reinterpret_cast<u4*>(p));
 }
-
-constexpr int kTok = 32;  // tokens (or slots) per workgroup
 
 // ----------------------------------------------------------------------------- scatter
 // Token-walking layout shared by scatter and gather+pool backward: a thread owns 8 columns
