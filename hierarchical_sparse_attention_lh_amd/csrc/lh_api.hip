@@ -302,7 +302,11 @@ lh::AttnCall layer_call(const Levels& L, float scale, const int32_t* gmap, const
 extern "C" {
 
 const char* lh_status_string(lh_status s) {
-  switch (s) {
+  // a C caller may pass any int: read it as one (an enum-typed load of a value outside the
+  // enumerators is undefined in C++)
+  int code;
+  memcpy(&code, &s, sizeof(code));
+  switch (code) {
     case LH_OK: return "ok";
     case LH_ERR_NULL: return "a required pointer is NULL";
     case LH_ERR_SHAPE: return "shape out of range or p^(L-1) does not divide N";
