@@ -164,6 +164,7 @@ struct Tile {
 struct LaneStage {
   uint32_t row;    // the lane's row within each load's RPL rows
   uint32_t chunk;  // byte offset of the lane's swizzled 16-byte piece within its row
+  uint32_t wofs;   // byte offset of the wave's 1 KB within each load's 4 KB of LDS (uniform)
 };
 
 template <int D>
@@ -172,12 +173,17 @@ __device__ __forceinline__ LaneStage lane_stage(int wave, int lane) {
   LaneStage ls;
   ls.row = static_cast<uint32_t>(lane / CPR);
   ls.chunk = static_cast<uint32_t>(((lane % CPR) ^ rkey<D>(wave * RPL + lane / CPR)) << 4);
+  ls.wofs = __builtin_amdgcn_readfirstlane(wave * 1024);
   return ls;
 }
 
-// LDS destination of load i: each wave instruction fills 1 KB of contiguous LDS.
-__device__ __forceinline__ uint16_t* lds_dst(uint16_t* lds, int i, int wave) {
-  return lds + (i * 4 + wave) * 64 * 8;
+typedef __attribute__((address_space(3))) char* lds_bytes;
+
+// LDS destination of load i: each wave instruction fills 1 KB of contiguous LDS.  The address
+// is built from scalar values only (the buffer's fixed LDS address, the load index and the
+// wave's uniform offset), so it reaches M0 without a per-load vector-to-scalar move.
+__device__ __forceinline__ lds_bytes lds_dst(uint16_t* lds, int i, const LaneStage& ls) {
+  return (lds_bytes)lds + i * 4096 + ls.wofs;
 }
 
 // Stage rows row0 .. row0 + ROWS - 1 of a strided operand.  A whole tile inside the sequence
@@ -194,15 +200,18 @@ __device__ __forceinline__ void stage_strided(const HeadRows& hr, const LaneStag
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       const char* base = hr.x + static_cast<int64_t>(row0 + i * 4 * T::RPL) * hr.rsb;
-      __builtin_amdgcn_global_load_lds(base + o, lds_dst(lds, i, wave), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(base + o, lds_dst(lds, i, ls), 16, 0, 0);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       const int row = min(row0 + (i * 4 + wave) * T::RPL + static_cast<int>(ls.row), S - 1);
       const char* g = hr.x + static_cast<int64_t>(row) * hr.rsb + ls.chunk;
-      __builtin_amdgcn_global_load_lds(g, lds_dst(lds, i, wave), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(g, lds_dst(lds, i, ls), 16, 0, 0);
     }
+    // (an empty statement after the loads: otherwise the compiler merges the last load of
+    // both branches into one after them, on a per-lane 64-bit address)
+    asm volatile("");
   }
 }
 
@@ -227,7 +236,7 @@ __device__ __forceinline__ void stage_mapped(const HeadRows& hr, const LaneStage
         static_cast<uint64_t>(static_cast<uint32_t>(id[i])) * hr.rsb + ls.chunk;
     const int64_t dp = id[i] >= hr.n0 ? hr.dp : 0;
     const char* g = hr.x + static_cast<int64_t>(rel) + dp;
-    __builtin_amdgcn_global_load_lds(g, lds_dst(lds, i, wave), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g, lds_dst(lds, i, ls), 16, 0, 0);
   }
 }
 
@@ -240,20 +249,39 @@ __device__ __forceinline__ void mapped_offsets(const int* id, uint32_t rsb, cons
                                                uint32_t* o) {
 #pragma unroll
   for (int i = 0; i < Tile<ROWS, D>::LOADS; ++i) {
-    o[i] = static_cast<uint32_t>(id[i]) * rsb + ls.chunk;
+    // ids and row strides below 2^24 (the launcher's condition for this mode): a 24-bit
+    // multiply-add is exact here
+    o[i] = __umul24(static_cast<uint32_t>(id[i]), rsb) + ls.chunk;
     asm volatile("" : "+v"(o[i]));
   }
 }
 
-template <int ROWS, int D>
-__device__ __forceinline__ void stage_mapped32(const HeadRows& hr, const uint32_t* o,
-                                               uint16_t* lds, int wave) {
+template <int ROWS, int D, bool TWO = true>
+__device__ __forceinline__ void stage_mapped32(const HeadRows& hr, const LaneStage& ls,
+                                               const uint32_t* o, uint16_t* lds) {
 #pragma unroll
   for (int i = 0; i < Tile<ROWS, D>::LOADS; ++i) {
-    // (the instruction offset of a direct global->LDS load moves the LDS address too, so it
-    // stays 0 everywhere)
-    const char* base = o[i] < hr.n0b ? hr.x : hr.pn;
-    __builtin_amdgcn_global_load_lds(base + o[i], lds_dst(lds, i, wave), 16, 0, 0);
+    if constexpr (!TWO) {
+      // one load on a per-lane 64-bit address (fewer live registers)
+      const char* base = o[i] < hr.n0b ? hr.x : hr.pn;
+      __builtin_amdgcn_global_load_lds(base + o[i], lds_dst(lds, i, ls), 16, 0, 0);
+      continue;
+    }
+    // Each lane loads from one of two uniform bases: two exec-masked loads, each a scalar
+    // base plus the 32-bit lane offset.  The opaque copies keep each address sum inside its
+    // branch, and the empty statement after one load keeps the compiler from merging the two
+    // into one load on a per-lane 64-bit address.  (The instruction offset of a direct
+    // global->LDS load moves the LDS address too, so it stays 0 everywhere.)
+    const lds_bytes dst = lds_dst(lds, i, ls);
+    uint32_t oo = o[i];
+    if (oo < hr.n0b) {
+      asm volatile("" : "+v"(oo));
+      __builtin_amdgcn_global_load_lds(hr.x + oo, dst, 16, 0, 0);
+    } else {
+      asm volatile("" : "+v"(oo));
+      __builtin_amdgcn_global_load_lds(hr.pn + oo, dst, 16, 0, 0);
+      asm volatile("");
+    }
   }
 }
 
@@ -482,10 +510,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
       int idk[NL];
       if (sk) get_ids(t + 2, idk);
       load_ids(t + 3);
-      if (sv) stage_mapped32<BN, D>(hv, vo, odd ? vs0 : vs1, wave);
+      if (sv) stage_mapped32<BN, D>(hv, ls, vo, odd ? vs0 : vs1);
       if (sk) {
         mapped_offsets<BN, D>(idk, hk.rsb, ls, vo);
-        stage_mapped32<BN, D>(hk, vo, odd ? ks1 : ks0, wave);
+        stage_mapped32<BN, D>(hk, ls, vo, odd ? ks1 : ks0);
       }
     } else {
       int idk[NL], idv[NL];
@@ -575,8 +603,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
       if constexpr (MODE == 1) {
         uint32_t o[NL];
         mapped_offsets<BN, D>(id, hk.rsb, ls, o);
-        stage_mapped32<BN, D>(hk, o, B1 ? ks0 : ks1, wave);
-        stage_mapped32<BN, D>(hv, o, B1 ? vs0 : vs1, wave);
+        stage_mapped32<BN, D>(hk, ls, o, B1 ? ks0 : ks1);
+        stage_mapped32<BN, D>(hv, ls, o, B1 ? vs0 : vs1);
       } else {
         stage_k(t + 1, id, B1 ? ks0 : ks1);
         stage_v(t + 1, id, B1 ? vs0 : vs1);
@@ -604,11 +632,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
       if constexpr (MODE == 1) {
         uint32_t o0[NL];
         mapped_offsets<BN, D>(id0, hk.rsb, ls, o0);
-        stage_mapped32<BN, D>(hk, o0, ks0, wave);
-        stage_mapped32<BN, D>(hv, o0, vs0, wave);
+        stage_mapped32<BN, D>(hk, ls, o0, ks0);
+        stage_mapped32<BN, D>(hv, ls, o0, vs0);
         if (nkt > 1) {
           mapped_offsets<BN, D>(id1, hk.rsb, ls, vo);
-          stage_mapped32<BN, D>(hk, vo, ks1, wave);
+          stage_mapped32<BN, D>(hk, ls, vo, ks1);
         }
       } else {
         stage_k(0, id0, ks0);
@@ -636,8 +664,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
       if constexpr (MODE == 1) {
         uint32_t o0[NL];
         mapped_offsets<BN, D>(id0, hk.rsb, ls, o0);
-        stage_mapped32<BN, D>(hk, o0, ks0, wave);
-        stage_mapped32<BN, D>(hv, o0, vs0, wave);
+        stage_mapped32<BN, D>(hk, ls, o0, ks0);
+        stage_mapped32<BN, D>(hv, ls, o0, vs0);
       } else {
         stage_k(0, id0, ks0);
         stage_v(0, id0, vs0);
@@ -784,7 +812,7 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
     if constexpr (MODE == 1) {
       uint32_t o[Tile<BQ, D>::LOADS];
       mapped_offsets<BQ, D>(id, hq.rsb, ls, o);
-      stage_mapped32<BQ, D>(hq, o, B1 ? qs1 : qs0, wave);
+      stage_mapped32<BQ, D>(hq, ls, o, B1 ? qs1 : qs0);
     } else if constexpr (MODE == 2) {
       stage_mapped<BQ, D>(hq, ls, id, B1 ? qs1 : qs0, wave);
     } else {
@@ -1184,8 +1212,9 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
     if constexpr (MODE == 1) {
       uint32_t o[Tile<BN, D>::LOADS];
       mapped_offsets<BN, D>(id, hk.rsb, ls, o);
-      stage_mapped32<BN, D>(hk, o, B1 ? ks1 : ks0, wave);
-      stage_mapped32<BN, D>(hv, o, B1 ? vs1 : vs0, wave);
+      // (D = 128: the two-base form would push this kernel past its register budget)
+      stage_mapped32<BN, D, D == 64>(hk, ls, o, B1 ? ks1 : ks0);
+      stage_mapped32<BN, D, D == 64>(hv, ls, o, B1 ? vs1 : vs0);
     } else if constexpr (MODE == 2) {
       stage_mapped<BN, D>(hk, ls, id, B1 ? ks1 : ks0, wave);
       stage_mapped<BN, D>(hv, ls, id, B1 ? vs1 : vs0, wave);
@@ -1377,12 +1406,14 @@ RowSrc mapped_rows(const Levels& lv, const void* x, const void* px) {
 
 // ------------------------------------------------------------------------ launchers
 // Mapped calls use 32-bit row offsets when every pyramid row of a head (N + P1 rows of
-// H * D bf16) lies within 4 GiB of the head's first raw row.
+// H * D bf16) lies within 4 GiB of the head's first raw row, and ids and the row stride stay
+// below 2^24 (the offsets are 24-bit products).
 int mapped_mode(const AttnCall& c) {
   if (!c.mapped) return 0;
   const int64_t rows = c.lv->N + c.lv->P1;
   const int64_t rsb = static_cast<int64_t>(c.lv->H) * c.lv->D * 2;
-  return rows * rsb < (int64_t(1) << 32) ? 1 : 2;
+  const int64_t lim24 = int64_t(1) << 24;
+  return rows * rsb < (int64_t(1) << 32) && rows <= lim24 && rsb < lim24 ? 1 : 2;
 }
 
 hipError_t launch_attn_fwd2(const AttnCall& c, const void* q, const void* k, const void* v,
