@@ -741,12 +741,13 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
   constexpr int BK = 128, NB = BQ / 32;
   using QT = Tile<BQ, D>;
   constexpr int NL = QT::LOADS;
-  // each buffer its own LDS object, named statically (the loop is unrolled by two): the
-  // compiler then does not make a tile's LDS reads wait for the next tile's loads
-  __shared__ __attribute__((aligned(16))) uint16_t qs0[BQ * D], qs1[BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t ds0[BQ * D], ds1[BQ * D];
-  __shared__ __attribute__((aligned(16))) float ls0[BQ], ls1[BQ];
-  __shared__ __attribute__((aligned(16))) float dl0[BQ], dl1[BQ];
+  // each buffer its own LDS object, named statically (the loop is unrolled by the number of
+  // buffers): the compiler then does not make a tile's LDS reads wait for the next tile's
+  // loads.  The pipelined D = 64 loop rotates three buffers, the others two.
+  __shared__ __attribute__((aligned(16))) uint16_t qs0[BQ * D], qs1[BQ * D], qs2[BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t ds0[BQ * D], ds1[BQ * D], ds2[BQ * D];
+  __shared__ __attribute__((aligned(16))) float ls0[BQ], ls1[BQ], ls2[BQ];
+  __shared__ __attribute__((aligned(16))) float dl0[BQ], dl1[BQ], dl2[BQ];
   __shared__ __attribute__((aligned(16))) int32_t idr[4][BQ];
 
   const int S = a.S, Sp = a.Sp;
@@ -801,10 +802,29 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
     if constexpr (MAPPED)
       if (wave == 0 && t < nqt) stage_words(gm + t * BQ, idr[t & 3], lane, BQ);
   };
-  // Tile t: Q rows (through the map), dO rows, lse and Delta into buffer B1; the ids are read
+  // buffer `bi` (a compile-time index) of each kind
+  auto qbuf = [&](auto bi) -> uint16_t* {
+    constexpr int B = decltype(bi)::value;
+    if constexpr (B == 0) return qs0; else if constexpr (B == 1) return qs1; else return qs2;
+  };
+  auto dbuf = [&](auto bi) -> uint16_t* {
+    constexpr int B = decltype(bi)::value;
+    if constexpr (B == 0) return ds0; else if constexpr (B == 1) return ds1; else return ds2;
+  };
+  auto lbuf = [&](auto bi) -> float* {
+    constexpr int B = decltype(bi)::value;
+    if constexpr (B == 0) return ls0; else if constexpr (B == 1) return ls1; else return ls2;
+  };
+  auto dlbuf = [&](auto bi) -> float* {
+    constexpr int B = decltype(bi)::value;
+    if constexpr (B == 0) return dl0; else if constexpr (B == 1) return dl1; else return dl2;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  // Tile t: Q rows (through the map), dO rows, lse and Delta into buffer bufc; the ids are read
   // from LDS before any load of this step is issued.
   auto stage = [&](int t, auto bufc) {
-    constexpr bool B1 = decltype(bufc)::value;
     const int q0 = t * BQ;
     int id[NL];
     if constexpr (MAPPED) ids_of<BQ, D>(idr[t & 3], ls, wave, id);
@@ -812,24 +832,23 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
     if constexpr (MODE == 1) {
       uint32_t o[Tile<BQ, D>::LOADS];
       mapped_offsets<BQ, D>(id, hq.rsb, ls, o);
-      stage_mapped32<BQ, D>(hq, ls, o, B1 ? qs1 : qs0);
+      stage_mapped32<BQ, D>(hq, ls, o, qbuf(bufc));
     } else if constexpr (MODE == 2) {
-      stage_mapped<BQ, D>(hq, ls, id, B1 ? qs1 : qs0, wave);
+      stage_mapped<BQ, D>(hq, ls, id, qbuf(bufc), wave);
     } else {
-      stage_strided<BQ, D>(hq, ls, q0, S, B1 ? qs1 : qs0, wave);
+      stage_strided<BQ, D>(hq, ls, q0, S, qbuf(bufc), wave);
     }
-    stage_strided<BQ, D>(hd, ls, q0, S, B1 ? ds1 : ds0, wave);
-    if (wave == 0) stage_words(lb + q0, B1 ? ls1 : ls0, lane, BQ);
-    if (wave == 1) stage_words(dlb + q0, B1 ? dl1 : dl0, lane, BQ);
+    stage_strided<BQ, D>(hd, ls, q0, S, dbuf(bufc), wave);
+    if (wave == 0) stage_words(lb + q0, lbuf(bufc), lane, BQ);
+    if (wave == 1) stage_words(dlb + q0, dlbuf(bufc), lane, BQ);
   };
 
   // generic tile (any D, BQ): S and dP per 32-query block, then dV and dK per 16-query chunk
   auto tile = [&](auto masked, int t, auto bufc) {
-    constexpr bool B1 = decltype(bufc)::value;
-    const uint16_t* qsb = B1 ? qs1 : qs0;
-    const uint16_t* dsb = B1 ? ds1 : ds0;
-    const float* lsb = B1 ? ls1 : ls0;
-    const float* dlb_ = B1 ? dl1 : dl0;
+    const uint16_t* qsb = qbuf(bufc);
+    const uint16_t* dsb = dbuf(bufc);
+    const float* lsb = lbuf(bufc);
+    const float* dlb_ = dlbuf(bufc);
     const int q0 = t * BQ;
     f32x16 sacc[NB], pacc[NB];
 #pragma unroll
@@ -888,13 +907,16 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
     }
   };
 
-  // D = 64, 64 queries: twelve groups of four MFMAs (A: S and dP of one 32-query block, two k
-  // steps; V / K: the dV or dK update of one 16-query chunk), each carrying vector work whose
-  // inputs are complete:
-  //   A00 -          A01 -            A10 b0 b1     A11 p0 d0     V0 p1   K0 d1
-  //   V1 b2 b3       K1 p2 d2         V2 p3         K2 d3         V3 -    K3 -
-  // (b = exp and dS of chunk t4, p / d = hi-lo split of P / dS of chunk t4), fixed with
-  // scheduling barriers; the LDS operands of each group are read one group ahead.
+  // D = 64, 64 queries, pipelined across tiles: twelve groups of four MFMAs, each carrying one
+  // unit of vector work whose inputs are complete:
+  //   A0 p3'   A1 d3'   V3' b0   K3' b1   A2 p0   A3 d0   V0 p1   K0 d1   V1 b2   K1 p2   V2 d2   K2 b3
+  // (A0 .. A3: S and dP of one 32-query block, two k steps each; V / K: the dV or dK update of
+  // one 16-query chunk; b = exp and dS of a chunk, p / d = hi-lo split of its P / dS; ' = the
+  // previous tile).  The split and the dV / dK products of a tile's last chunk run in the next
+  // tile's first four groups, so no group is left without vector work; that tile's Q and dO
+  // rows are still in their LDS buffers then, because three buffers rotate (a buffer is
+  // restaged only two steps after its tile).  Fixed with scheduling barriers; the LDS operands
+  // of each group are read one group ahead.  S and dP stay in sacc / pacc across steps.
   uint32_t loff[4], tro[2][2];
 #pragma unroll
   for (int j = 0; j < 4; ++j) loff[j] = op_off<64>(lq, hl, j);
@@ -902,19 +924,21 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
   for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
     for (int sec = 0; sec < 2; ++sec) tro[d2][sec] = tr_off<64>(lane, d2, sec);
+  f32x16 sacc[2], pacc[2];
 
-  auto tile64 = [&](auto masked, int t, auto bufc) {
+  auto tile64p = [&](auto masked, int t, auto cur, auto prev, auto first) {
     constexpr bool MASK = decltype(masked)::value;
-    constexpr bool B1 = decltype(bufc)::value;
+    constexpr bool FIRST = decltype(first)::value;
     const int q0 = t * BQ;
-    const uint16_t* qsb = B1 ? qs1 : qs0;
-    const uint16_t* dsb = B1 ? ds1 : ds0;
-    const float* lsb = B1 ? ls1 : ls0;
-    const float* dlb_ = B1 ? dl1 : dl0;
-    f32x16 sacc[2], pacc[2];
+    const uint16_t* qsb = qbuf(cur);
+    const uint16_t* dsb = dbuf(cur);
+    const uint16_t* qsp = qbuf(prev);
+    const uint16_t* dsp = dbuf(prev);
+    const float* lsb = lbuf(cur);
+    const float* dlb_ = dlbuf(cur);
     bf16x8 op[12][4];
-    float4 lsv[2][4];
-    bf16x8 ph[4], pl[4], sh[4], sl[4];
+    float4 lsv[4][2];
+    bf16x8 ph[3], pl[3], sh[3], sl[3], php, plp, shp, slp;
     // opaque copies: the address sums stay inside the loop and fold into instruction
     // offsets instead of being hoisted into dozens of live registers
     uint32_t lo[4], tr[2][2];
@@ -930,62 +954,79 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
         tr[d2][sec] = tro[d2][sec];
         asm volatile("" : "+v"(tr[d2][sec]));
       }
-    auto rd = [&](const uint16_t* tile_base, int m, int j) {
-      return lds_at(tile_base, 4096 * m + lo[j]);
-    };
-    auto load_ops = [&](auto uc) {
-      constexpr int u = decltype(uc)::value;
-      if constexpr (u < 4) {
-        constexpr int b2 = u >> 1, kh = u & 1;
+    // group g's MFMA unit: A units at g = 0, 1, 4, 5; dV units at even g >= 2 and dK units at
+    // odd g >= 3, for chunk 3 of the previous tile (g = 2, 3) or chunk (g - 6) / 2 of this one
+    auto is_a = [](int g) { return g == 0 || g == 1 || g == 4 || g == 5; };
+    auto load_ops = [&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (g == 0 || g == 1 || g == 4 || g == 5) {
+        constexpr int b2 = g >> 2, kh = g & 1;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int kk = 2 * kh + j;
-          op[u][2 * j] = rd(qsb, b2, kk);
-          op[u][2 * j + 1] = rd(dsb, b2, kk);
+          op[g][2 * j] = lds_at(qsb, 4096 * b2 + lo[kk]);
+          op[g][2 * j + 1] = lds_at(dsb, 4096 * b2 + lo[kk]);
         }
-      } else {
-        constexpr int c = u - 4, t4 = c >> 1;
-        const uint16_t* src = (c & 1) ? qsb : dsb;
+      } else if constexpr (!(FIRST && (g == 2 || g == 3))) {
+        constexpr int t4 = g < 4 ? 3 : (g - 6) >> 1;
+        const uint16_t* src = (g & 1) ? (g < 4 ? qsp : qsb) : (g < 4 ? dsp : dsb);
 #pragma unroll
         for (int d2 = 0; d2 < 2; ++d2)
-          op[u][d2] = tr_op(src, 2048 * t4 + tr[d2][0], 2048 * t4 + tr[d2][1]);
+          op[g][d2] = tr_op(src, 2048 * t4 + tr[d2][0], 2048 * t4 + tr[d2][1]);
       }
     };
-    auto mfma_unit = [&](auto uc) {
-      constexpr int u = decltype(uc)::value;
-      if constexpr (u < 4) {
-        constexpr int b2 = u >> 1, kh = u & 1;
+    auto mfma_unit = [&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (g == 0 || g == 1 || g == 4 || g == 5) {
+        constexpr int b2 = g >> 2, kh = g & 1;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int kk = 2 * kh + j;
-          sacc[b2] = mfma32(op[u][2 * j], kreg[kk], sacc[b2]);
-          pacc[b2] = mfma32(op[u][2 * j + 1], vreg[kk], pacc[b2]);
+          sacc[b2] = mfma32(op[g][2 * j], kreg[kk], sacc[b2]);
+          pacc[b2] = mfma32(op[g][2 * j + 1], vreg[kk], pacc[b2]);
         }
-      } else if constexpr (((u - 4) & 1) == 0) {
-        constexpr int t4 = (u - 4) >> 1;
+      } else if constexpr (FIRST && (g == 2 || g == 3)) {
+      } else if constexpr ((g & 1) == 0) {
+        const bf16x8& h_ = g == 2 ? php : ph[(g - 6) >> 1];
+        const bf16x8& l_ = g == 2 ? plp : pl[(g - 6) >> 1];
 #pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2) dvacc[d2] = mfma32(op[u][d2], pl[t4], dvacc[d2]);
+        for (int d2 = 0; d2 < 2; ++d2) dvacc[d2] = mfma32(op[g][d2], l_, dvacc[d2]);
 #pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2) dvacc[d2] = mfma32(op[u][d2], ph[t4], dvacc[d2]);
+        for (int d2 = 0; d2 < 2; ++d2) dvacc[d2] = mfma32(op[g][d2], h_, dvacc[d2]);
       } else {
-        constexpr int t4 = (u - 4) >> 1;
+        const bf16x8& h_ = g == 3 ? shp : sh[(g - 7) >> 1];
+        const bf16x8& l_ = g == 3 ? slp : sl[(g - 7) >> 1];
 #pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2) dkacc[d2] = mfma32(op[u][d2], sl[t4], dkacc[d2]);
+        for (int d2 = 0; d2 < 2; ++d2) dkacc[d2] = mfma32(op[g][d2], l_, dkacc[d2]);
 #pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2) dkacc[d2] = mfma32(op[u][d2], sh[t4], dkacc[d2]);
+        for (int d2 = 0; d2 < 2; ++d2) dkacc[d2] = mfma32(op[g][d2], h_, dkacc[d2]);
       }
     };
-    auto load_ls = [&](int b2) {
+    (void)is_a;
+    // the lse values of chunk t4's queries, read one group before its b unit
+    auto load_ls = [&](int t4) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        lsv[b2][g] = *reinterpret_cast<const float4*>(&lsb[b2 * 32 + g * 8 + hl * 4]);
+      for (int gg = 0; gg < 2; ++gg)
+        lsv[t4][gg] = *reinterpret_cast<const float4*>(
+            &lsb[(t4 >> 1) * 32 + ((t4 & 1) * 2 + gg) * 8 + hl * 4]);
+    };
+    auto seed = [&](int b2) {
+      sacc[b2] = zero16();
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 d4 = *reinterpret_cast<const float4*>(&dlb_[b2 * 32 + g * 8 + hl * 4]);
+        pacc[b2][4 * g] = d4.x;
+        pacc[b2][4 * g + 1] = d4.y;
+        pacc[b2][4 * g + 2] = d4.z;
+        pacc[b2][4 * g + 3] = d4.w;
+      }
     };
     auto b_unit = [&](int t4) {
       const int b2 = t4 >> 1, half = t4 & 1;
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
         const int g = 2 * half + gg;
-        const float lv4[4] = {lsv[b2][g].x, lsv[b2][g].y, lsv[b2][g].z, lsv[b2][g].w};
+        const float lv4[4] = {lsv[t4][gg].x, lsv[t4][gg].y, lsv[t4][gg].z, lsv[t4][gg].w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = g * 4 + u;
@@ -1001,111 +1042,155 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
     };
     auto sp_unit = [&](int t4) { c_to_op2(sacc[t4 >> 1], t4 & 1, ph[t4], pl[t4]); };
     auto sd_unit = [&](int t4) { c_to_op2(pacc[t4 >> 1], t4 & 1, sh[t4], sl[t4]); };
-    auto layout = [&](auto nvc) {
-      constexpr int nv = decltype(nvc)::value;
+    // one group: nm MFMAs, each followed by nv vector instructions, with the group's LDS
+    // reads (the next group's operands) right after its first MFMA: the wait that the first
+    // MFMA needs then covers only reads issued a whole group earlier, and the new reads have
+    // the rest of the group to land
+    auto layout = [&](auto nmc, auto nvc) {
+      constexpr int nm = decltype(nmc)::value, nv = decltype(nvc)::value;
+      if constexpr (nm > 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
+        for (int i = 0; i < nm; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+          if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
-    using N0 = std::integral_constant<int, 0>;
-    using N6 = std::integral_constant<int, 6>;
-    using N12 = std::integral_constant<int, 12>;
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-    using I4 = std::integral_constant<int, 4>;
-    using I5 = std::integral_constant<int, 5>;
-    using I6 = std::integral_constant<int, 6>;
-    using I7 = std::integral_constant<int, 7>;
-    using I8 = std::integral_constant<int, 8>;
-    using I9 = std::integral_constant<int, 9>;
-    using I10 = std::integral_constant<int, 10>;
-    using I11 = std::integral_constant<int, 11>;
-    auto seed = [&](int b2) {
-      sacc[b2] = zero16();
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 d4 = *reinterpret_cast<const float4*>(&dlb_[b2 * 32 + g * 8 + hl * 4]);
-        pacc[b2][4 * g] = d4.x;
-        pacc[b2][4 * g + 1] = d4.y;
-        pacc[b2][4 * g + 2] = d4.z;
-        pacc[b2][4 * g + 3] = d4.w;
-      }
-    };
+    using G0 = std::integral_constant<int, 0>;
+    using G1 = std::integral_constant<int, 1>;
+    using G2 = std::integral_constant<int, 2>;
+    using G3 = std::integral_constant<int, 3>;
+    using G4 = std::integral_constant<int, 4>;
+    using G5 = std::integral_constant<int, 5>;
+    using G6 = std::integral_constant<int, 6>;
+    using G7 = std::integral_constant<int, 7>;
+    using G8 = std::integral_constant<int, 8>;
+    using G9 = std::integral_constant<int, 9>;
+    using G10 = std::integral_constant<int, 10>;
+    using G11 = std::integral_constant<int, 11>;
+    using M0 = std::integral_constant<int, 0>;
+    using M4 = std::integral_constant<int, 4>;
+    using V0 = std::integral_constant<int, 0>;
+    using V6 = std::integral_constant<int, 6>;
+    using MP = std::conditional_t<FIRST, M0, M4>;  // previous tile's MFMA groups
+    using VP = std::conditional_t<FIRST, V0, V6>;  // previous tile's vector work
     seed(0);
-    load_ops(I0{});
+    load_ops(G0{});
     __builtin_amdgcn_sched_barrier(0);
-    load_ops(I1{});
-    mfma_unit(I0{});
-    layout(N0{});
-    load_ops(I2{});
-    seed(1);
+    // g0: A0 | p3'
+    load_ops(G1{});
+    mfma_unit(G0{});
+    if constexpr (!FIRST) c_to_op2(sacc[1], 1, php, plp);
+    layout(M4{}, VP{});
+    // g1: A1 | d3'
+    load_ops(G2{});
     load_ls(0);
-    mfma_unit(I1{});
-    layout(N0{});
-    load_ops(I3{});
-    mfma_unit(I2{});
-    b_unit(0);
-    b_unit(1);
-    layout(N12{});
-    load_ops(I4{});
-    mfma_unit(I3{});
-    sp_unit(0);
-    sd_unit(0);
-    layout(N12{});
-    load_ops(I5{});
+    mfma_unit(G1{});
+    if constexpr (!FIRST) c_to_op2(pacc[1], 1, shp, slp);
+    layout(M4{}, VP{});
+    // g2: V3' | b0   (block 1 of the previous tile is consumed: seed it for this tile)
+    load_ops(G3{});
     load_ls(1);
-    mfma_unit(I4{});
+    seed(1);
+    mfma_unit(G2{});
+    b_unit(0);
+    layout(MP{}, V6{});
+    // g3: K3' | b1
+    load_ops(G4{});
+    mfma_unit(G3{});
+    b_unit(1);
+    layout(MP{}, V6{});
+    // g4: A2 | p0
+    load_ops(G5{});
+    mfma_unit(G4{});
+    sp_unit(0);
+    layout(M4{}, V6{});
+    // g5: A3 | d0
+    load_ops(G6{});
+    mfma_unit(G5{});
+    sd_unit(0);
+    layout(M4{}, V6{});
+    // g6: V0 | p1
+    load_ops(G7{});
+    mfma_unit(G6{});
     sp_unit(1);
-    layout(N6{});
-    load_ops(I6{});
-    mfma_unit(I5{});
+    layout(M4{}, V6{});
+    // g7: K0 | d1
+    load_ops(G8{});
+    load_ls(2);
+    mfma_unit(G7{});
     sd_unit(1);
-    layout(N6{});
-    load_ops(I7{});
-    mfma_unit(I6{});
+    layout(M4{}, V6{});
+    // g8: V1 | b2
+    load_ops(G9{});
+    mfma_unit(G8{});
     b_unit(2);
-    b_unit(3);
-    layout(N12{});
-    load_ops(I8{});
-    mfma_unit(I7{});
+    layout(M4{}, V6{});
+    // g9: K1 | p2
+    load_ops(G10{});
+    mfma_unit(G9{});
     sp_unit(2);
+    layout(M4{}, V6{});
+    // g10: V2 | d2
+    load_ops(G11{});
+    load_ls(3);
+    mfma_unit(G10{});
     sd_unit(2);
-    layout(N12{});
-    load_ops(I9{});
-    mfma_unit(I8{});
-    sp_unit(3);
-    layout(N6{});
-    load_ops(I10{});
-    mfma_unit(I9{});
-    sd_unit(3);
-    layout(N6{});
-    load_ops(I11{});
-    mfma_unit(I10{});
-    layout(N0{});
-    mfma_unit(I11{});
-    layout(N0{});
+    layout(M4{}, V6{});
+    // g11: K2 | b3   (chunk 3's split and products run in the next step, or in finish)
+    mfma_unit(G11{});
+    b_unit(3);
+    layout(M4{}, V6{});
   };
 
-  auto step = [&](int t, auto bufc) {
-    if (t + 1 < nqt) stage(t + 1, std::integral_constant<bool, !decltype(bufc)::value>{});
+  // the last tile's chunk 3: split, dV and dK (its rows are still in buffer bi)
+  auto finish = [&](auto bi) {
+    bf16x8 hi, lo_;
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2) {
+      const bf16x8 ao = tr_op(dbuf(bi), 2048 * 3 + tro[d2][0], 2048 * 3 + tro[d2][1]);
+      c_to_op2(sacc[1], 1, hi, lo_);
+      dvacc[d2] = mfma32(ao, lo_, dvacc[d2]);
+      dvacc[d2] = mfma32(ao, hi, dvacc[d2]);
+    }
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2) {
+      const bf16x8 aq = tr_op(qbuf(bi), 2048 * 3 + tro[d2][0], 2048 * 3 + tro[d2][1]);
+      c_to_op2(pacc[1], 1, hi, lo_);
+      dkacc[d2] = mfma32(aq, lo_, dkacc[d2]);
+      dkacc[d2] = mfma32(aq, hi, dkacc[d2]);
+    }
+  };
+
+  auto next_buf = [](auto bi) {
+    return std::integral_constant<int, (decltype(bi)::value + 1) % 3>{};
+  };
+  // pipelined step t (D = 64): tile t in buffer cur, tile t - 1 in prev, tile t + 1 staged
+  // into the third buffer
+  auto step3 = [&](int t, auto cur, auto prev, auto first) {
+    if (t + 1 < nqt) stage(t + 1, next_buf(cur));
     const int q0 = t * BQ;
     const bool msk = (causal && q0 < kw + 31) || q0 + BQ > S;
-    if constexpr (D == 64 && BQ == 64) {
-      if (msk)
-        tile64(std::true_type{}, t, bufc);
-      else
-        tile64(std::false_type{}, t, bufc);
-    } else {
-      if (msk)
-        tile(std::true_type{}, t, bufc);
-      else
-        tile(std::false_type{}, t, bufc);
-    }
+    if (msk)
+      tile64p(std::true_type{}, t, cur, prev, first);
+    else
+      tile64p(std::false_type{}, t, cur, prev, first);
+    wait_vmem();
+    __syncthreads();
+  };
+  // generic step t: tile t in buffer bufc, tile t + 1 staged into the other of two buffers
+  auto step = [&](int t, auto bufc) {
+    if (t + 1 < nqt) stage(t + 1, std::integral_constant<int, 1 - decltype(bufc)::value>{});
+    const int q0 = t * BQ;
+    const bool msk = (causal && q0 < kw + 31) || q0 + BQ > S;
+    if (msk)
+      tile(std::true_type{}, t, bufc);
+    else
+      tile(std::false_type{}, t, bufc);
     wait_vmem();
     __syncthreads();
   };
@@ -1113,15 +1198,32 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
     load_ids(qt0);
     wait_vmem();
     __syncthreads();
-    stage(qt0, std::false_type{});
+    stage(qt0, I0{});
   }
   wait_vmem();
   __syncthreads();
-  for (int t = qt0; t < nqt; t += 2) {
-    step(t, std::false_type{});
-    if (t + 1 < nqt) step(t + 1, std::true_type{});
+  if constexpr (D == 64 && BQ == 64) {
+    if (qt0 < nqt) {
+      step3(qt0, I0{}, I2{}, std::true_type{});
+      for (int t = qt0 + 1; t < nqt; t += 3) {
+        step3(t, I1{}, I0{}, std::false_type{});
+        if (t + 1 < nqt) step3(t + 1, I2{}, I1{}, std::false_type{});
+        if (t + 2 < nqt) step3(t + 2, I0{}, I2{}, std::false_type{});
+      }
+      const int lastb = (nqt - 1 - qt0) % 3;
+      if (lastb == 0)
+        finish(I0{});
+      else if (lastb == 1)
+        finish(I1{});
+      else
+        finish(I2{});
+    }
+  } else {
+    for (int t = qt0; t < nqt; t += 2) {
+      step(t, I0{});
+      if (t + 1 < nqt) step(t + 1, I1{});
+    }
   }
-
   if (mykey < a.g_rows) {
     float* dkr = a.dk + b * a.gsb + h * a.gsh + static_cast<int64_t>(mykey) * a.gss;
     float* dvr = a.dv + b * a.gsb + h * a.gsh + static_cast<int64_t>(mykey) * a.gss;
