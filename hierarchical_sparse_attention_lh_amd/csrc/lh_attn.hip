@@ -416,16 +416,13 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     constexpr bool odd = decltype(par)::value;
     const uint16_t* vsb = odd ? vs1 : vs0;
     const uint16_t* ksn = odd ? ks0 : ks1;
+    // the next tile's K operands now; the V^T operands are read during the score products
+    // below, so the first product waits only for the K reads
     bf16x8 ka[2][D / 16], va[4][D / 32];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2) ka[b2][kk] = lds_at(ksn, b2 * 64 * D + op_off<D>(lq, hl, kk));
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        va[t4][db] = tr_op(vsb, t4 * 32 * D + toff[db][0], t4 * 32 * D + toff[db][1]);
     if constexpr (decltype(masked)::value) mask(t, sacc);
     float mx = sacc[0][0];
 #pragma unroll
@@ -449,16 +446,22 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     constexpr int EPC = 32 / NS;       // exponentials per chunk
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) nxt[b2] = zero16();
+    constexpr int NV = 4 * (D / 32);   // V^T operands of the tile
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int kk = i >> 1, b2 = i & 1;
       nxt[b2] = mfma32(ka[b2][kk], qreg[kk], nxt[b2]);
+      if (i < NV) {
+        const int t4 = i / (D / 32), db = i % (D / 32);
+        va[t4][db] = tr_op(vsb, t4 * 32 * D + toff[db][0], t4 * 32 * D + toff[db][1]);
+      }
 #pragma unroll
       for (int u = 0; u < EPC; ++u) {
         const int e = i * EPC + u, eb = e >> 4, er = e & 15;
         sacc[eb][er] = __builtin_amdgcn_exp2f(fmaf(sacc[eb][er], sl2, -m_run));
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 2 * EPC, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
