@@ -404,6 +404,31 @@ def test_attention_forward(seq, d):
     _check_fwd(o, lse, x, True, [(0, 0), (0, 1)], d)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_with_a_late_score_beyond_float_range(d):
+    """Head 0: every query lies along e1 and one key in a later tile has a score of 1024, far
+    above every score of the first tile (184 apart in base 2 after the scale, beyond float's
+    exponent range): exponentials taken against an early row maximum would overflow, so the
+    forward's running maximum must move.  Both passes of the backward use the saved
+    log-sum-exp.  All against the float64 oracle."""
+    seq = 300
+    x = _attn_case(seq, d, seed=11 + d)
+    q, k = x["q"].float(), x["k"].float()
+    q[0, 0] = 0.0
+    q[0, 0, :, 0] = 16.0 * (d / 64) ** 0.5  # about the same scaled score at both head sizes
+    k[0, 0, 200] = 0.0
+    k[0, 0, 200, 0] = 64.0
+    x["q"], x["k"] = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    rng = np.random.default_rng(5)
+    dout = torch.from_numpy(rng.standard_normal((1, 2, seq, d)).astype(np.float32)).to(torch.bfloat16)
+    qd, kd, vd, dod = (t.to(DEV) for t in (x["q"], x["k"], x["v"], dout))
+    o, lse = ops.lh_attn_fwd(qd, kd, vd)
+    grads = ops.lh_attn_bwd(qd, kd, vd, o, lse, dod)
+    torch.cuda.synchronize()
+    _check_fwd(o, lse, x, True, [(0, 0), (0, 1)], d)
+    _check_bwd(grads, x, dout, True, [(0, 0), (0, 1)], d)
+
+
 @pytest.mark.parametrize("seq,d", [(100, 64), (1000, 64), (777, 128), (640, 64), (6000, 64)])
 def test_attention_backward(seq, d):
     x = _attn_case(seq, d, seed=seq * 3 + d)
