@@ -1150,6 +1150,240 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
     layout(M4{}, V6{});
   };
 
+  // D = 128, 32 queries (one wave per SIMD, so the wave's own instruction stream must keep
+  // the MFMAs busy): the dV / dK products of a tile run in the next tile, beside that tile's
+  // score products, exponentials and splits.  Twelve groups of four MFMAs:
+  //   A0 c0'  A1 c1'  A2 c2'  A3 c3'  V0a' b0  V0b' b1  K0a' p0  K0b' d0  V1a' p1  V1b' d1  K1a'  K1b'
+  // (A0 .. A3: S and dP, two k steps each; V / K: dV or dK of one 16-query chunk, two
+  // 32-column blocks; b = exp and dS of a chunk, p / d = hi-lo split of its P / dS; c' = copy
+  // of the previous tile's split operands, so this tile's splits can take their registers;
+  // ' = the previous tile, whose Q and dO rows are still staged: three buffers rotate).
+  uint32_t loff128[8], tro128[4][2];
+  if constexpr (D == 128) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) loff128[j] = op_off<128>(lq, hl, j);
+#pragma unroll
+    for (int d2 = 0; d2 < 4; ++d2)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) tro128[d2][sec] = tr_off<128>(lane, d2, sec);
+  }
+  f32x16 sacc1, pacc1;
+  bf16x8 phc[2], plc[2], shc[2], slc[2];  // this tile's split P and dS, chunks 0 and 1
+  bf16x8 php[2], plp[2], shp[2], slp[2];  // the previous tile's
+
+  auto tile128p = [&](auto masked, int t, auto cur, auto prev, auto first) {
+    constexpr bool MASK = decltype(masked)::value;
+    constexpr bool FIRST = decltype(first)::value;
+    const int q0 = t * BQ;
+    const uint16_t* qsb = qbuf(cur);
+    const uint16_t* dsb = dbuf(cur);
+    const uint16_t* qsp = qbuf(prev);
+    const uint16_t* dsp = dbuf(prev);
+    const float* lsb = lbuf(cur);
+    const float* dlb_ = dlbuf(cur);
+    bf16x8 op[12][4];
+    float4 lsv[2][2];
+    uint32_t lo[8], tr[4][2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lo[j] = loff128[j];
+      asm volatile("" : "+v"(lo[j]));
+    }
+#pragma unroll
+    for (int d2 = 0; d2 < 4; ++d2)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        tr[d2][sec] = tro128[d2][sec];
+        asm volatile("" : "+v"(tr[d2][sec]));
+      }
+    // group g: A units at g < 4 (k steps 2g, 2g + 1); at g >= 4, u = g - 4 picks chunk u / 4,
+    // dV (u / 2 even) or dK, and the column blocks 0-1 or 2-3 (u odd)
+    auto load_ops = [&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (g < 4) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          op[g][2 * j] = lds_at(qsb, lo[2 * g + j]);
+          op[g][2 * j + 1] = lds_at(dsb, lo[2 * g + j]);
+        }
+      } else if constexpr (!FIRST) {
+        constexpr int u = g - 4, c = u >> 2, isk = (u >> 1) & 1, half = u & 1;
+        const uint16_t* src = isk ? qsp : dsp;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int d2 = 2 * half + i;
+          op[g][i] = tr_op(src, 4096 * c + tr[d2][0], 4096 * c + tr[d2][1]);
+        }
+      }
+    };
+    auto mfma_unit = [&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (g < 4) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          sacc1 = mfma32(op[g][2 * j], kreg[2 * g + j], sacc1);
+          pacc1 = mfma32(op[g][2 * j + 1], vreg[2 * g + j], pacc1);
+        }
+      } else if constexpr (!FIRST) {
+        constexpr int u = g - 4, c = u >> 2, isk = (u >> 1) & 1, half = u & 1;
+        const bf16x8& h_ = isk ? shp[c] : php[c];
+        const bf16x8& l_ = isk ? slp[c] : plp[c];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          f32x16& acc = isk ? dkacc[2 * half + i] : dvacc[2 * half + i];
+          acc = mfma32(op[g][i], l_, acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          f32x16& acc = isk ? dkacc[2 * half + i] : dvacc[2 * half + i];
+          acc = mfma32(op[g][i], h_, acc);
+        }
+      }
+    };
+    auto seed = [&]() {
+      sacc1 = zero16();
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 d4 = *reinterpret_cast<const float4*>(&dlb_[g * 8 + hl * 4]);
+        pacc1[4 * g] = d4.x;
+        pacc1[4 * g + 1] = d4.y;
+        pacc1[4 * g + 2] = d4.z;
+        pacc1[4 * g + 3] = d4.w;
+      }
+    };
+    auto load_ls = [&](int t4) {
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+        lsv[t4][gg] = *reinterpret_cast<const float4*>(&lsb[(t4 * 2 + gg) * 8 + hl * 4]);
+    };
+    auto b_unit = [&](int t4) {
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int g = 2 * t4 + gg;
+        const float lv4[4] = {lsv[t4][gg].x, lsv[t4][gg].y, lsv[t4][gg].z, lsv[t4][gg].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = g * 4 + u;
+          float p = __builtin_amdgcn_exp2f(fmaf(sacc1[r], sl2, -lv4[u]));
+          if constexpr (MASK) {
+            const int qa = q0 + g * 8 + hl * 4 + u;
+            if ((causal && qa < mykey) || qa >= S) p = 0.f;
+          }
+          sacc1[r] = p;
+          pacc1[r] = p * pacc1[r];
+        }
+      }
+    };
+    auto copy_unit = [&](int k) {  // the previous tile's split operands into their registers
+      const int c = k >> 1;
+      if (k & 1) {
+        shp[c] = shc[c];
+        slp[c] = slc[c];
+      } else {
+        php[c] = phc[c];
+        plp[c] = plc[c];
+      }
+    };
+    auto layout = [&](auto nmc, auto nvc) {
+      constexpr int nm = decltype(nmc)::value, nv = decltype(nvc)::value;
+      if constexpr (nm > 0) {
+#pragma unroll
+        for (int i = 0; i < nm; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+          if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using G0 = std::integral_constant<int, 0>;
+    using G1 = std::integral_constant<int, 1>;
+    using G2 = std::integral_constant<int, 2>;
+    using G3 = std::integral_constant<int, 3>;
+    using G4 = std::integral_constant<int, 4>;
+    using G5 = std::integral_constant<int, 5>;
+    using G6 = std::integral_constant<int, 6>;
+    using G7 = std::integral_constant<int, 7>;
+    using G8 = std::integral_constant<int, 8>;
+    using G9 = std::integral_constant<int, 9>;
+    using G10 = std::integral_constant<int, 10>;
+    using G11 = std::integral_constant<int, 11>;
+    using M0 = std::integral_constant<int, 0>;
+    using M4 = std::integral_constant<int, 4>;
+    using V0 = std::integral_constant<int, 0>;
+    using V2 = std::integral_constant<int, 2>;
+    using V6 = std::integral_constant<int, 6>;
+    using MP = std::conditional_t<FIRST, M0, M4>;  // previous tile's MFMA groups
+    using VC = std::conditional_t<FIRST, V0, V2>;  // copies of the previous tile's operands
+    seed();
+    load_ops(G0{});
+    __builtin_amdgcn_sched_barrier(0);
+    load_ops(G1{});
+    mfma_unit(G0{});
+    if constexpr (!FIRST) copy_unit(0);
+    layout(M4{}, VC{});
+    load_ops(G2{});
+    mfma_unit(G1{});
+    if constexpr (!FIRST) copy_unit(1);
+    layout(M4{}, VC{});
+    load_ops(G3{});
+    mfma_unit(G2{});
+    if constexpr (!FIRST) copy_unit(2);
+    layout(M4{}, VC{});
+    load_ops(G4{});
+    load_ls(0);
+    mfma_unit(G3{});
+    if constexpr (!FIRST) copy_unit(3);
+    layout(M4{}, VC{});
+    load_ops(G5{});
+    load_ls(1);
+    mfma_unit(G4{});
+    b_unit(0);
+    layout(MP{}, V6{});
+    load_ops(G6{});
+    mfma_unit(G5{});
+    b_unit(1);
+    layout(MP{}, V6{});
+    load_ops(G7{});
+    mfma_unit(G6{});
+    c_to_op2(sacc1, 0, phc[0], plc[0]);
+    layout(MP{}, V6{});
+    load_ops(G8{});
+    mfma_unit(G7{});
+    c_to_op2(pacc1, 0, shc[0], slc[0]);
+    layout(MP{}, V6{});
+    load_ops(G9{});
+    mfma_unit(G8{});
+    c_to_op2(sacc1, 1, phc[1], plc[1]);
+    layout(MP{}, V6{});
+    load_ops(G10{});
+    mfma_unit(G9{});
+    c_to_op2(pacc1, 1, shc[1], slc[1]);
+    layout(MP{}, V6{});
+    load_ops(G11{});
+    mfma_unit(G10{});
+    layout(MP{}, V0{});
+    mfma_unit(G11{});
+    layout(MP{}, V0{});
+  };
+
+  // D = 128: the last tile's dV and dK products (its rows are still in buffer bi)
+  auto finish128 = [&](auto bi) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int d2 = 0; d2 < 4; ++d2) {
+        const bf16x8 ao = tr_op(dbuf(bi), 4096 * c + tro128[d2][0], 4096 * c + tro128[d2][1]);
+        dvacc[d2] = mfma32(ao, plc[c], dvacc[d2]);
+        dvacc[d2] = mfma32(ao, phc[c], dvacc[d2]);
+        const bf16x8 aq = tr_op(qbuf(bi), 4096 * c + tro128[d2][0], 4096 * c + tro128[d2][1]);
+        dkacc[d2] = mfma32(aq, slc[c], dkacc[d2]);
+        dkacc[d2] = mfma32(aq, shc[c], dkacc[d2]);
+      }
+  };
+
   // the last tile's chunk 3: split, dV and dK (its rows are still in buffer bi)
   auto finish = [&](auto bi) {
     bf16x8 hi, lo_;
@@ -1178,10 +1412,17 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
     if (t + 1 < nqt) stage(t + 1, next_buf(cur));
     const int q0 = t * BQ;
     const bool msk = (causal && q0 < kw + 31) || q0 + BQ > S;
-    if (msk)
-      tile64p(std::true_type{}, t, cur, prev, first);
-    else
-      tile64p(std::false_type{}, t, cur, prev, first);
+    if constexpr (D == 64) {
+      if (msk)
+        tile64p(std::true_type{}, t, cur, prev, first);
+      else
+        tile64p(std::false_type{}, t, cur, prev, first);
+    } else {
+      if (msk)
+        tile128p(std::true_type{}, t, cur, prev, first);
+      else
+        tile128p(std::false_type{}, t, cur, prev, first);
+    }
     wait_vmem();
     __syncthreads();
   };
@@ -1205,7 +1446,10 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
   }
   wait_vmem();
   __syncthreads();
-  if constexpr (D == 64 && BQ == 64) {
+  if constexpr ((D == 64 && BQ == 64) || (D == 128 && BQ == 32)) {
+    auto fin = [&](auto bi) {
+      if constexpr (D == 64) finish(bi); else finish128(bi);
+    };
     if (qt0 < nqt) {
       step3(qt0, I0{}, I2{}, std::true_type{});
       for (int t = qt0 + 1; t < nqt; t += 3) {
@@ -1215,11 +1459,11 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
       }
       const int lastb = (nqt - 1 - qt0) % 3;
       if (lastb == 0)
-        finish(I0{});
+        fin(I0{});
       else if (lastb == 1)
-        finish(I1{});
+        fin(I1{});
       else
-        finish(I2{});
+        fin(I2{});
     }
   } else {
     for (int t = qt0; t < nqt; t += 2) {
