@@ -307,7 +307,7 @@ struct FwdArgs {
 };
 
 // MODE: 0 = strided rows, 1 = mapped rows with 32-bit offsets, 2 = mapped rows, 64-bit.
-template <int D, bool PIPE, int MODE>
+template <int D, int MODE>
 __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
   constexpr bool MAPPED = MODE != 0;
   constexpr int BM = 128, BN = 64;
@@ -379,24 +379,6 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     if constexpr (MODE == 2) stage_mapped<BN, D>(hv, ls, id, lds, wave);
     else stage_strided<BN, D>(hv, ls, t * BN, S, lds, wave);
   };
-  // MODE 1: offsets of the tile whose V rows the next step stages (its K rows were staged
-  // with the same offsets one step earlier)
-  uint32_t vo[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i) vo[i] = 0;
-
-  // S^T of one key tile: 32 keys x 32 queries per C block, two blocks.
-  auto scores = [&](f32x16 (&sacc)[2], auto bufc) {
-    const uint16_t* ksb = decltype(bufc)::value ? ks1 : ks0;
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) {
-      sacc[b2] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        sacc[b2] = mfma32(lds_at(ksb, b2 * 64 * D + op_off<D>(lq, hl, kk)), qreg[kk], sacc[b2]);
-    }
-  };
-
   auto mask = [&](int t, f32x16 (&sacc)[2]) {
     const int k0 = t * BN;
 #pragma unroll
@@ -408,134 +390,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
       }
   };
 
-  // Online softmax of score tile t and its P V^T product, with the score product of tile t+1
-  // (into nxt, from K buffer !odd) woven into the same instruction stream: short chunks of one
-  // MFMA plus some vector work, fixed by scheduling barriers, so one wave's vector work runs
-  // beside the other wave's MFMAs.
-  auto soft_pv = [&](auto masked, int t, f32x16 (&sacc)[2], f32x16 (&nxt)[2], auto par) {
-    constexpr bool odd = decltype(par)::value;
-    const uint16_t* vsb = odd ? vs1 : vs0;
-    const uint16_t* ksn = odd ? ks0 : ks1;
-    // the next tile's K operands now; the V^T operands are read during the score products
-    // below, so the first product waits only for the K reads
-    bf16x8 ka[2][D / 16], va[4][D / 32];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) ka[b2][kk] = lds_at(ksn, b2 * 64 * D + op_off<D>(lq, hl, kk));
-    if constexpr (decltype(masked)::value) mask(t, sacc);
-    float mx = sacc[0][0];
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[b2][r]);
-    mx = pair_max(mx) * sl2;
-    const bool grow = mx > m_run + kSlack;
-    if (__any(grow)) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      l_run *= alpha;
-      l_cmp *= alpha;
-      m_run = m_new;
-    }
-    constexpr int NS = 2 * (D / 16);  // score MFMAs per tile
-    constexpr int EPC = 32 / NS;       // exponentials per chunk
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) nxt[b2] = zero16();
-    constexpr int NV = 4 * (D / 32);   // V^T operands of the tile
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int kk = i >> 1, b2 = i & 1;
-      nxt[b2] = mfma32(ka[b2][kk], qreg[kk], nxt[b2]);
-      if (i < NV) {
-        const int t4 = i / (D / 32), db = i % (D / 32);
-        va[t4][db] = tr_op(vsb, t4 * 32 * D + toff[db][0], t4 * 32 * D + toff[db][1]);
-      }
-#pragma unroll
-      for (int u = 0; u < EPC; ++u) {
-        const int e = i * EPC + u, eb = e >> 4, er = e & 15;
-        sacc[eb][er] = __builtin_amdgcn_exp2f(fmaf(sacc[eb][er], sl2, -m_run));
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2 * EPC, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    bf16x8 ph[4], pl[4];
-    c_to_op2(sacc[0], 0, ph[0], pl[0]);
-    float part[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) part[r] = sacc[0][r] + sacc[1][r];
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32(va[t4][db], pl[t4], oacc[db]);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32(va[t4][db], ph[t4], oacc[db]);
-      if (t4 < 3) c_to_op2(sacc[(t4 + 1) >> 1], (t4 + 1) & 1, ph[t4 + 1], pl[t4 + 1]);
-      if (t4 == 0) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) part[r] += part[r + 8];
-      } else if (t4 == 1) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part[r] += part[r + 4];
-      } else if (t4 == 2) {
-        part[0] += part[2];
-        part[1] += part[3];
-        part[0] += part[1];
-      } else {
-        const float yk = part[0] - l_cmp;
-        const float tk = l_run + yk;
-        l_cmp = (tk - l_run) - yk;
-        l_run = tk;
-      }
-#pragma unroll
-      for (int i = 0; i < 2 * (D / 32); ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // Pipelined step t: LDS holds K(t+1) and V(t); K(t+2) and V(t+1) are loaded into the
-  // buffers freed by step t-1, the ids of tile t+3 into the ring.  The ids are read from LDS
-  // before this step issues any load, so no read waits on a load still in flight.
-  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto par) {
-    constexpr bool odd = decltype(par)::value;
-    const bool sk = t + 2 < nkt, sv = t + 1 < nkt;
-    if constexpr (MODE == 1) {
-      int idk[NL];
-      if (sk) get_ids(t + 2, idk);
-      load_ids(t + 3);
-      if (sv) stage_mapped32<BN, D>(hv, ls, vo, odd ? vs0 : vs1);
-      if (sk) {
-        mapped_offsets<BN, D>(idk, hk.rsb, ls, vo);
-        stage_mapped32<BN, D>(hk, ls, vo, odd ? ks1 : ks0);
-      }
-    } else {
-      int idk[NL], idv[NL];
-      if (sk) get_ids(t + 2, idk);
-      if (sv) get_ids(t + 1, idv);
-      load_ids(t + 3);
-      if (sk) stage_k(t + 2, idk, odd ? ks1 : ks0);
-      if (sv) stage_v(t + 1, idv, odd ? vs0 : vs1);
-    }
-    const int k0 = t * BN;
-    if ((causal && k0 + BN - 1 > qw) || k0 + BN > S)
-      soft_pv(std::true_type{}, t, cur, nxt, par);
-    else
-      soft_pv(std::false_type{}, t, cur, nxt, par);
-    wait_vmem();
-    __syncthreads();
-  };
-
-  // Plain tile (D = 128, two waves per SIMD): S^T = K Q^T, online softmax, O^T += V^T P^T.
+  // Tile t: S^T = K Q^T, online softmax, O^T += V^T P^T (hi-lo P).
   auto plain_tile = [&](auto masked, int t, auto bufc) {
     constexpr bool B1 = decltype(bufc)::value;
     const uint16_t* ksb = B1 ? ks1 : ks0;
@@ -622,64 +477,28 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     __syncthreads();
   };
 
-  if constexpr (PIPE) {
-    load_ids(0);
-    load_ids(1);
-    load_ids(2);
-    wait_vmem();
-    __syncthreads();
-    {
-      int id0[NL], id1[NL];
-      get_ids(0, id0);
-      if (nkt > 1) get_ids(1, id1);
-      if constexpr (MODE == 1) {
-        uint32_t o0[NL];
-        mapped_offsets<BN, D>(id0, hk.rsb, ls, o0);
-        stage_mapped32<BN, D>(hk, ls, o0, ks0);
-        stage_mapped32<BN, D>(hv, ls, o0, vs0);
-        if (nkt > 1) {
-          mapped_offsets<BN, D>(id1, hk.rsb, ls, vo);
-          stage_mapped32<BN, D>(hk, ls, vo, ks1);
-        }
-      } else {
-        stage_k(0, id0, ks0);
-        stage_v(0, id0, vs0);
-        if (nkt > 1) stage_k(1, id1, ks1);
-      }
+  load_ids(0);
+  load_ids(1);
+  wait_vmem();
+  __syncthreads();
+  {
+    int id0[NL];
+    get_ids(0, id0);
+    if constexpr (MODE == 1) {
+      uint32_t o0[NL];
+      mapped_offsets<BN, D>(id0, hk.rsb, ls, o0);
+      stage_mapped32<BN, D>(hk, ls, o0, ks0);
+      stage_mapped32<BN, D>(hv, ls, o0, vs0);
+    } else {
+      stage_k(0, id0, ks0);
+      stage_v(0, id0, vs0);
     }
-    wait_vmem();
-    __syncthreads();
-    f32x16 sa[2], sb[2];
-    scores(sa, std::false_type{});
-    __syncthreads();  // K(0)'s buffer is refilled by the first step
-    for (int t = 0; t < nkt; t += 2) {
-      step(t, sa, sb, std::false_type{});
-      if (t + 1 < nkt) step(t + 1, sb, sa, std::true_type{});
-    }
-  } else {
-    load_ids(0);
-    load_ids(1);
-    wait_vmem();
-    __syncthreads();
-    {
-      int id0[NL];
-      get_ids(0, id0);
-      if constexpr (MODE == 1) {
-        uint32_t o0[NL];
-        mapped_offsets<BN, D>(id0, hk.rsb, ls, o0);
-        stage_mapped32<BN, D>(hk, ls, o0, ks0);
-        stage_mapped32<BN, D>(hv, ls, o0, vs0);
-      } else {
-        stage_k(0, id0, ks0);
-        stage_v(0, id0, vs0);
-      }
-    }
-    wait_vmem();
-    __syncthreads();
-    for (int t = 0; t < nkt; t += 2) {
-      plain_step(t, std::false_type{});
-      if (t + 1 < nkt) plain_step(t + 1, std::true_type{});
-    }
+  }
+  wait_vmem();
+  __syncthreads();
+  for (int t = 0; t < nkt; t += 2) {
+    plain_step(t, std::false_type{});
+    if (t + 1 < nkt) plain_step(t + 1, std::true_type{});
   }
 
   const float l_own = l_run - l_cmp;
@@ -699,19 +518,18 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
   if (hl == 0) a.lse[bh * Sp + myq] = m_run + log2f(l_tot);  // base-2 log-sum-exp
 }
 
-// Two waves per SIMD: the pipelined loop at D = 64, the plain loop at D = 128 (the pipeline's
-// extra registers would force one wave there, which cannot hide its vector work).
-#define LH_FWD(NAME, D, PIPE, MODE)                                                          \
-  __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void NAME( \
+// Three waves per SIMD at D = 64 (about 145 registers), two at D = 128.
+#define LH_FWD(NAME, D, MODE, W)                                                             \
+  __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W))) void NAME( \
       FwdArgs a) {                                                                          \
-    attn_fwd_body<D, PIPE, MODE>(a);                                                        \
+    attn_fwd_body<D, MODE>(a);                                                              \
   }
-LH_FWD(attn_fwd_d64, 64, true, 0)
-LH_FWD(attn_fwd_d128, 128, false, 0)
-LH_FWD(attn_fwd_mapped_d64, 64, true, 1)
-LH_FWD(attn_fwd_mapped_d128, 128, false, 1)
-LH_FWD(attn_fwd_mapped64_d64, 64, true, 2)
-LH_FWD(attn_fwd_mapped64_d128, 128, false, 2)
+LH_FWD(attn_fwd_d64, 64, 0, 3)
+LH_FWD(attn_fwd_d128, 128, 0, 2)
+LH_FWD(attn_fwd_mapped_d64, 64, 1, 3)
+LH_FWD(attn_fwd_mapped_d128, 128, 1, 2)
+LH_FWD(attn_fwd_mapped64_d64, 64, 2, 3)
+LH_FWD(attn_fwd_mapped64_d128, 128, 2, 2)
 #undef LH_FWD
 
 // ------------------------------------------------------------------------ backward
