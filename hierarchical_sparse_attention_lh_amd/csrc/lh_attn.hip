@@ -398,11 +398,15 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     f32x16 sacc[2];
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) sacc[b2] = zero16();
+    // at D = 64 (three waves per SIMD) the matrix products run at raised wave priority, so
+    // that a wave with MFMAs to issue goes ahead of the other waves' softmax work
+    if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2)
         sacc[b2] = mfma32(lds_at(ksb, b2 * 64 * D + op_off<D>(lq, hl, kk)), qreg[kk], sacc[b2]);
+    if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
     if constexpr (decltype(masked)::value) mask(t, sacc);
     float mx = sacc[0][0];
 #pragma unroll
@@ -438,6 +442,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     const float tk = l_run + yk;
     l_cmp = (tk - l_run) - yk;
     l_run = tk;
+    if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       bf16x8 ph, pl;
@@ -449,6 +454,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
         oacc[db] = mfma32(av, ph, oacc[db]);
       }
     }
+    if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
   };
 
   auto plain_step = [&](int t, auto bufc) {
