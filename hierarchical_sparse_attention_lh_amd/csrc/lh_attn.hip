@@ -814,15 +814,15 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
         }
       } else if constexpr (FIRST && (g == 2 || g == 3)) {
       } else if constexpr ((g & 1) == 0) {
-        const bf16x8& h_ = g == 2 ? php : ph[(g - 6) >> 1];
-        const bf16x8& l_ = g == 2 ? plp : pl[(g - 6) >> 1];
+        const bf16x8& h_ = g == 2 ? php : ph[g == 2 ? 0 : (g - 6) >> 1];
+        const bf16x8& l_ = g == 2 ? plp : pl[g == 2 ? 0 : (g - 6) >> 1];
 #pragma unroll
         for (int d2 = 0; d2 < 2; ++d2) dvacc[d2] = mfma32(op[g][d2], l_, dvacc[d2]);
 #pragma unroll
         for (int d2 = 0; d2 < 2; ++d2) dvacc[d2] = mfma32(op[g][d2], h_, dvacc[d2]);
       } else {
-        const bf16x8& h_ = g == 3 ? shp : sh[(g - 7) >> 1];
-        const bf16x8& l_ = g == 3 ? slp : sl[(g - 7) >> 1];
+        const bf16x8& h_ = g == 3 ? shp : sh[g == 3 ? 0 : (g - 7) >> 1];
+        const bf16x8& l_ = g == 3 ? slp : sl[g == 3 ? 0 : (g - 7) >> 1];
 #pragma unroll
         for (int d2 = 0; d2 < 2; ++d2) dkacc[d2] = mfma32(op[g][d2], l_, dkacc[d2]);
 #pragma unroll
@@ -1318,17 +1318,17 @@ __device__ __forceinline__ void attn_bwd_kv_body(const BwdArgs& a) {
 // -------------------------------------------------------------- query pass (dQ)
 // Workgroup = 128 queries (the forward's layout) over key tiles of BN: S^T = K Q^T and
 // dP^T = V dO^T (K and V rows staged), dS^T feeds dQ^T = K^T dS^T as the B operand, with K^T
-// read from the staged K rows by transposing reads.
+// read from the staged K rows by transposing reads.  One 32-key block at a time, so the
+// kernel fits three waves per SIMD at D = 64.
 template <int D, int BN, int MODE>
 __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
   constexpr bool MAPPED = MODE != 0;
   constexpr int BM = 128, NBK = BN / 32;
   using KT = Tile<BN, D>;
   constexpr int NL = KT::LOADS;
-  // each buffer its own LDS object, named statically (the loop is unrolled by the number of
-  // buffers); the pipelined D = 64 loop rotates three buffers, the others two
-  __shared__ __attribute__((aligned(16))) uint16_t ks0[BN * D], ks1[BN * D], ks2[BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs0[BN * D], vs1[BN * D], vs2[BN * D];
+  // each buffer its own LDS object, named statically (the loop is unrolled by two)
+  __shared__ __attribute__((aligned(16))) uint16_t ks0[BN * D], ks1[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs0[BN * D], vs1[BN * D];
   __shared__ __attribute__((aligned(16))) int32_t idr[4][BN];
 
   const int S = a.S, Sp = a.Sp;
@@ -1381,16 +1381,13 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
   };
   // buffer `bi` (a compile-time index) of each kind
   auto kbuf = [&](auto bi) -> uint16_t* {
-    constexpr int B = decltype(bi)::value;
-    if constexpr (B == 0) return ks0; else if constexpr (B == 1) return ks1; else return ks2;
+    if constexpr (decltype(bi)::value == 0) return ks0; else return ks1;
   };
   auto vbuf = [&](auto bi) -> uint16_t* {
-    constexpr int B = decltype(bi)::value;
-    if constexpr (B == 0) return vs0; else if constexpr (B == 1) return vs1; else return vs2;
+    if constexpr (decltype(bi)::value == 0) return vs0; else return vs1;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
   auto stage = [&](int t, auto bufc) {
     int id[NL];
     if constexpr (MAPPED) ids_of<BN, D>(idr[t & 3], ls, wave, id);
@@ -1410,6 +1407,9 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
     }
   };
 
+  // Tile t, one 32-key block at a time: S^T and dP^T, then dS^T, then its hi-lo split and the
+  // dQ^T update.  At D = 64 (three waves per SIMD) the matrix products run at raised wave
+  // priority, so a wave with MFMAs to issue goes ahead of the other waves' vector work.
   auto tile = [&](auto masked, int t, auto bufc) {
     const uint16_t* ksb = kbuf(bufc);
     const uint16_t* vsb = vbuf(bufc);
@@ -1420,251 +1420,48 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
       ko[j] = koff[j];
       asm volatile("" : "+v"(ko[j]));
     }
-    f32x16 sacc[NBK], pacc[NBK];
 #pragma unroll
     for (int b2 = 0; b2 < NBK; ++b2) {
-      sacc[b2] = zero16();
+      f32x16 sacc = zero16(), pacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pacc[b2][r] = dlt;  // every C register is this lane's query
+      for (int r = 0; r < 16; ++r) pacc[r] = dlt;  // every C register is this lane's query
+      if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        sacc[b2] = mfma32(lds_at(ksb, b2 * 64 * D + ko[kk]), qreg[kk], sacc[b2]);
-        pacc[b2] = mfma32(lds_at(vsb, b2 * 64 * D + ko[kk]), oreg[kk], pacc[b2]);
+        sacc = mfma32(lds_at(ksb, b2 * 64 * D + ko[kk]), qreg[kk], sacc);
+        pacc = mfma32(lds_at(vsb, b2 * 64 * D + ko[kk]), oreg[kk], pacc);
       }
-    }
-    // pacc = Delta - dP, so P * pacc = -dS: one multiply; the sign goes into the final scale
-#pragma unroll
-    for (int b2 = 0; b2 < NBK; ++b2)
+      if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
+      // pacc = Delta - dP, so P * pacc = -dS: one multiply; the sign goes into the final scale
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(sacc[b2][r], sl2, -l2));
+        float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], sl2, -l2));
         if constexpr (decltype(masked)::value) {
           const int key = k0 + b2 * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
           if ((causal && key > myq) || key >= S) p = 0.f;
         }
-        pacc[b2][r] = p * pacc[b2][r];
+        pacc[r] = p * pacc[r];
       }
+      if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int t4 = 0; t4 < 2 * NBK; ++t4) {
-      bf16x8 sh, sl;
-      c_to_op2(pacc[t4 >> 1], t4 & 1, sh, sl);
+      for (int hh = 0; hh < 2; ++hh) {
+        const int t4 = 2 * b2 + hh;
+        bf16x8 sh, sl;
+        c_to_op2(pacc, hh, sh, sl);
 #pragma unroll
-      for (int d2 = 0; d2 < D / 32; ++d2) {
-        const uint32_t o0 = t4 * 32 * D + tr_off<D>(lane, d2, 0);
-        const uint32_t o1 = t4 * 32 * D + tr_off<D>(lane, d2, 1);
-        const bf16x8 ak = tr_op(ksb, o0, o1);
-        dqacc[d2] = mfma32(ak, sl, dqacc[d2]);
-        dqacc[d2] = mfma32(ak, sh, dqacc[d2]);
+        for (int d2 = 0; d2 < D / 32; ++d2) {
+          const uint32_t o0 = t4 * 32 * D + tr_off<D>(lane, d2, 0);
+          const uint32_t o1 = t4 * 32 * D + tr_off<D>(lane, d2, 1);
+          const bf16x8 ak = tr_op(ksb, o0, o1);
+          dqacc[d2] = mfma32(ak, sl, dqacc[d2]);
+          dqacc[d2] = mfma32(ak, sh, dqacc[d2]);
+        }
       }
+      if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
     }
   };
 
-  // D = 64, 64-key tiles, pipelined across tiles like the key pass: eight groups of four
-  // MFMAs, each carrying one unit of vector work whose inputs are complete:
-  //   A0 s2'   A1 s3'   Q2' b0   Q3' b1   A2 s0   A3 s1   Q0 b2   Q1 b3
-  // (A0 .. A3: S^T and dP^T of one 32-key block, two k steps each; Q: the dQ update of one
-  // 16-key chunk; b = exp and dS of a chunk, s = hi-lo split of its dS; ' = the previous
-  // tile).  The split and the dQ product of a tile's last two chunks run in the next tile's
-  // first four groups, reading that tile's K rows from its LDS buffer (three buffers rotate).
-  // Fixed with scheduling barriers; the LDS operands of each group are read one group ahead,
-  // right after the group's first MFMA.  dS of the last two chunks stays in pacc[1].
-  uint32_t trq[2][2];
-  if constexpr (D == 64 && BN == 64) {
-#pragma unroll
-    for (int d2 = 0; d2 < 2; ++d2)
-#pragma unroll
-      for (int sec = 0; sec < 2; ++sec) trq[d2][sec] = tr_off<64>(lane, d2, sec);
-  }
-  f32x16 sacc[2], pacc[2];
-
-  auto tile64q = [&](auto masked, int t, auto cur, auto prev, auto first) {
-    constexpr bool MASK = decltype(masked)::value;
-    constexpr bool FIRST = decltype(first)::value;
-    const int k0 = t * BN;
-    const uint16_t* ksb = kbuf(cur);
-    const uint16_t* vsb = vbuf(cur);
-    const uint16_t* ksp = kbuf(prev);
-    bf16x8 op[8][4];
-    bf16x8 sh[2], sl[2], shp[2], slp[2];
-    // opaque copies: the address sums stay inside the loop and fold into instruction offsets
-    uint32_t ko[4], tr[2][2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ko[j] = koff[j];
-      asm volatile("" : "+v"(ko[j]));
-    }
-#pragma unroll
-    for (int d2 = 0; d2 < 2; ++d2)
-#pragma unroll
-      for (int sec = 0; sec < 2; ++sec) {
-        tr[d2][sec] = trq[d2][sec];
-        asm volatile("" : "+v"(tr[d2][sec]));
-      }
-    // group g's MFMA unit: A units at g = 0, 1, 4, 5; dQ units for chunks 2, 3 of the
-    // previous tile at g = 2, 3 and for chunks 0, 1 of this one at g = 6, 7
-    auto load_ops = [&](auto gc) {
-      constexpr int g = decltype(gc)::value;
-      if constexpr (g == 0 || g == 1 || g == 4 || g == 5) {
-        constexpr int b2 = g >> 2, kh = g & 1;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int kk = 2 * kh + j;
-          op[g][2 * j] = lds_at(ksb, 4096 * b2 + ko[kk]);
-          op[g][2 * j + 1] = lds_at(vsb, 4096 * b2 + ko[kk]);
-        }
-      } else if constexpr (!(FIRST && g < 4)) {
-        constexpr int t4 = g < 4 ? g : g - 6;
-        const uint16_t* src = g < 4 ? ksp : ksb;
-#pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2)
-          op[g][d2] = tr_op(src, 2048 * t4 + tr[d2][0], 2048 * t4 + tr[d2][1]);
-      }
-    };
-    auto mfma_unit = [&](auto gc) {
-      constexpr int g = decltype(gc)::value;
-      if constexpr (g == 0 || g == 1 || g == 4 || g == 5) {
-        constexpr int b2 = g >> 2, kh = g & 1;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int kk = 2 * kh + j;
-          sacc[b2] = mfma32(op[g][2 * j], qreg[kk], sacc[b2]);
-          pacc[b2] = mfma32(op[g][2 * j + 1], oreg[kk], pacc[b2]);
-        }
-      } else if constexpr (FIRST && g < 4) {
-      } else {
-        constexpr int c = g < 4 ? g - 2 : g - 6;
-        const bf16x8& h_ = g < 4 ? shp[c] : sh[c];
-        const bf16x8& l_ = g < 4 ? slp[c] : sl[c];
-#pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2) dqacc[d2] = mfma32(op[g][d2], l_, dqacc[d2]);
-#pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2) dqacc[d2] = mfma32(op[g][d2], h_, dqacc[d2]);
-      }
-    };
-    auto seed = [&](int b2) {
-      sacc[b2] = zero16();
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pacc[b2][r] = dlt;  // every C register is this lane's query
-    };
-    // pacc = Delta - dP, so P * pacc = -dS: one multiply; the sign goes into the final scale
-    auto b_unit = [&](int t4) {
-      const int b2 = t4 >> 1, half = t4 & 1;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = half * 8 + i;
-        float p = __builtin_amdgcn_exp2f(fmaf(sacc[b2][r], sl2, -l2));
-        if constexpr (MASK) {
-          const int key = k0 + b2 * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-          if ((causal && key > myq) || key >= S) p = 0.f;
-        }
-        pacc[b2][r] = p * pacc[b2][r];
-      }
-    };
-    auto layout = [&](auto nmc, auto nvc) {
-      constexpr int nm = decltype(nmc)::value, nv = decltype(nvc)::value;
-      if constexpr (nm > 0) {
-#pragma unroll
-        for (int i = 0; i < nm; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-          if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
-        }
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    using G0 = std::integral_constant<int, 0>;
-    using G1 = std::integral_constant<int, 1>;
-    using G2 = std::integral_constant<int, 2>;
-    using G3 = std::integral_constant<int, 3>;
-    using G4 = std::integral_constant<int, 4>;
-    using G5 = std::integral_constant<int, 5>;
-    using G6 = std::integral_constant<int, 6>;
-    using G7 = std::integral_constant<int, 7>;
-    using M0 = std::integral_constant<int, 0>;
-    using M4 = std::integral_constant<int, 4>;
-    using V0 = std::integral_constant<int, 0>;
-    using V6 = std::integral_constant<int, 6>;
-    using MP = std::conditional_t<FIRST, M0, M4>;  // previous tile's MFMA groups
-    using VP = std::conditional_t<FIRST, V0, V6>;  // previous tile's vector work
-    seed(0);
-    load_ops(G0{});
-    __builtin_amdgcn_sched_barrier(0);
-    // g0: A0 | s2'
-    load_ops(G1{});
-    mfma_unit(G0{});
-    if constexpr (!FIRST) c_to_op2(pacc[1], 0, shp[0], slp[0]);
-    layout(M4{}, VP{});
-    // g1: A1 | s3'
-    load_ops(G2{});
-    mfma_unit(G1{});
-    if constexpr (!FIRST) c_to_op2(pacc[1], 1, shp[1], slp[1]);
-    layout(M4{}, VP{});
-    // g2: Q2' | b0   (block 1 of the previous tile is consumed: seed it for this tile)
-    load_ops(G3{});
-    seed(1);
-    mfma_unit(G2{});
-    b_unit(0);
-    layout(MP{}, V6{});
-    // g3: Q3' | b1
-    load_ops(G4{});
-    mfma_unit(G3{});
-    b_unit(1);
-    layout(MP{}, V6{});
-    // g4: A2 | s0
-    load_ops(G5{});
-    mfma_unit(G4{});
-    c_to_op2(pacc[0], 0, sh[0], sl[0]);
-    layout(M4{}, V6{});
-    // g5: A3 | s1
-    load_ops(G6{});
-    mfma_unit(G5{});
-    c_to_op2(pacc[0], 1, sh[1], sl[1]);
-    layout(M4{}, V6{});
-    // g6: Q0 | b2
-    load_ops(G7{});
-    mfma_unit(G6{});
-    b_unit(2);
-    layout(M4{}, V6{});
-    // g7: Q1 | b3   (chunks 2 and 3 are split and applied in the next step, or in finish)
-    mfma_unit(G7{});
-    b_unit(3);
-    layout(M4{}, V6{});
-  };
-
-  // the last tile's chunks 2 and 3: split and dQ (its K rows are still in buffer bi)
-  auto finish = [&](auto bi) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bf16x8 hi, lo_;
-      c_to_op2(pacc[1], c, hi, lo_);
-#pragma unroll
-      for (int d2 = 0; d2 < 2; ++d2) {
-        const bf16x8 ak =
-            tr_op(kbuf(bi), 2048 * (2 + c) + trq[d2][0], 2048 * (2 + c) + trq[d2][1]);
-        dqacc[d2] = mfma32(ak, lo_, dqacc[d2]);
-        dqacc[d2] = mfma32(ak, hi, dqacc[d2]);
-      }
-    }
-  };
-
-  auto next_buf = [](auto bi) {
-    return std::integral_constant<int, (decltype(bi)::value + 1) % 3>{};
-  };
-  // pipelined step t (D = 64): tile t in buffer cur, tile t - 1 in prev, tile t + 1 staged
-  // into the third buffer
-  auto step3 = [&](int t, auto cur, auto prev, auto first) {
-    if (t + 1 < nkt) stage(t + 1, next_buf(cur));
-    const int k0 = t * BN;
-    if ((causal && k0 + BN - 1 > qw) || k0 + BN > S)
-      tile64q(std::true_type{}, t, cur, prev, first);
-    else
-      tile64q(std::false_type{}, t, cur, prev, first);
-    wait_vmem();
-    __syncthreads();
-  };
-  // generic step t: tile t in buffer bufc, tile t + 1 staged into the other of two buffers
+  // step t: tile t in buffer bufc, tile t + 1 staged into the other of two buffers
   auto step = [&](int t, auto bufc) {
     if (t + 1 < nkt) stage(t + 1, std::integral_constant<int, 1 - decltype(bufc)::value>{});
     const int k0 = t * BN;
@@ -1681,27 +1478,9 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
   stage(0, I0{});
   wait_vmem();
   __syncthreads();
-  if constexpr (D == 64 && BN == 64) {
-    if (nkt > 0) {
-      step3(0, I0{}, I2{}, std::true_type{});
-      for (int t = 1; t < nkt; t += 3) {
-        step3(t, I1{}, I0{}, std::false_type{});
-        if (t + 1 < nkt) step3(t + 1, I2{}, I1{}, std::false_type{});
-        if (t + 2 < nkt) step3(t + 2, I0{}, I2{}, std::false_type{});
-      }
-      const int lastb = (nkt - 1) % 3;
-      if (lastb == 0)
-        finish(I0{});
-      else if (lastb == 1)
-        finish(I1{});
-      else
-        finish(I2{});
-    }
-  } else {
-    for (int t = 0; t < nkt; t += 2) {
-      step(t, I0{});
-      if (t + 1 < nkt) step(t + 1, I1{});
-    }
+  for (int t = 0; t < nkt; t += 2) {
+    step(t, I0{});
+    if (t + 1 < nkt) step(t + 1, I1{});
   }
 
   if (myq < a.g_rows) {
@@ -1720,14 +1499,15 @@ __device__ __forceinline__ void attn_bwd_q_body(const BwdArgs& a) {
   }
 }
 
-// Occupancy: at D = 64 both passes run two waves per SIMD; at D = 128 the query pass runs two
-// waves with 32-key tiles, the key pass one wave (its accumulators live in AGPRs).
+// Occupancy: at D = 64 the key pass runs two waves per SIMD and the query pass three; at
+// D = 128 the query pass runs two waves with 32-key tiles, the key pass one wave (its
+// accumulators live in AGPRs).
 #define LH_KV(NAME, D, BQ, MODE, ATTR)                                    \
   __global__ __launch_bounds__(256) ATTR void NAME(BwdArgs a) {           \
     attn_bwd_kv_body<D, BQ, MODE>(a);                                     \
   }
-#define LH_Q(NAME, D, BN, MODE)                                                            \
-  __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void NAME( \
+#define LH_Q(NAME, D, BN, MODE, W)                                                         \
+  __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W))) void NAME( \
       BwdArgs a) {                                                                         \
     attn_bwd_q_body<D, BN, MODE>(a);                                                       \
   }
@@ -1739,12 +1519,12 @@ LH_KV(attn_bwd_kv_mapped_d64, 64, 64, 1, LH_TWO_WAVES)
 LH_KV(attn_bwd_kv_mapped_d128, 128, 32, 1, LH_ONE_WAVE)
 LH_KV(attn_bwd_kv_mapped64_d64, 64, 64, 2, LH_TWO_WAVES)
 LH_KV(attn_bwd_kv_mapped64_d128, 128, 32, 2, LH_ONE_WAVE)
-LH_Q(attn_bwd_q_d64, 64, 64, 0)
-LH_Q(attn_bwd_q_d128, 128, 32, 0)
-LH_Q(attn_bwd_q_mapped_d64, 64, 64, 1)
-LH_Q(attn_bwd_q_mapped_d128, 128, 32, 1)
-LH_Q(attn_bwd_q_mapped64_d64, 64, 64, 2)
-LH_Q(attn_bwd_q_mapped64_d128, 128, 32, 2)
+LH_Q(attn_bwd_q_d64, 64, 64, 0, 3)
+LH_Q(attn_bwd_q_d128, 128, 32, 0, 2)
+LH_Q(attn_bwd_q_mapped_d64, 64, 64, 1, 3)
+LH_Q(attn_bwd_q_mapped_d128, 128, 32, 1, 2)
+LH_Q(attn_bwd_q_mapped64_d64, 64, 64, 2, 3)
+LH_Q(attn_bwd_q_mapped64_d128, 128, 32, 2, 2)
 #undef LH_KV
 #undef LH_Q
 #undef LH_TWO_WAVES
